@@ -1,0 +1,9 @@
+"""Seeded synthetic inputs shared by the CPU oracle and the HIP library's tests.
+
+This package holds no attention arithmetic: it only draws random tensors and applies the
+input constructions (duplicated key rows, an attention-sink key, a value grid) that the
+workloads call for.
+"""
+from .gen import CONFIGS, WorkloadConfig, make_inputs, randn_inputs, grid_inputs, tensor_digest
+
+__all__ = ["CONFIGS", "WorkloadConfig", "make_inputs", "randn_inputs", "grid_inputs", "tensor_digest"]

@@ -1,0 +1,140 @@
+"""Seeded bf16 input generators for the five attention workloads.
+
+Every tensor is drawn on the CPU with a ``torch.Generator`` seeded per workload, as float32,
+multiplied by the workload's sigma, and rounded to bfloat16 by torch's round-to-nearest-even
+cast.  Q, K, V and dO are drawn in that order.  The workloads stand in for the attention layers
+of the models the pages train (GPT-2 small/medium and LLaMA-7B shapes); no dataset or weight is
+involved.
+
+The module contains no softmax, no matmul and no gradient: only random draws and the input
+constructions below.
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+import math
+
+import numpy as np
+import torch
+
+# Entries of the tie-heavy grid: exact in bf16, and every dot product of two rows of length
+# <= 512 drawn from it is an exact multiple of 0.25 in fp32.
+GRID_VALUES = (-1.0, -0.5, 0.0, 0.5, 1.0)
+
+
+@dataclasses.dataclass(frozen=True)
+class WorkloadConfig:
+    cid: int
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    scale: float
+    modes: tuple
+    seed: int
+    sigma_qk: float = 1.0
+    kind: str = "randn"  # "randn" | "dup" | "sink" | "grid"
+
+    def with_shape(self, **kw) -> "WorkloadConfig":
+        return dataclasses.replace(self, **kw)
+
+
+def _inv_sqrt_f32(d: int) -> float:
+    return float(np.float32(1.0 / math.sqrt(d)))
+
+
+CONFIGS = {
+    1: WorkloadConfig(1, "tiny-dup", 1, 1, 128, 64, False, 0.125, (0, 1, 2), 1001, kind="dup"),
+    2: WorkloadConfig(2, "gpt2-small", 8, 12, 1024, 64, True, 0.125, (1, 2), 1002),
+    3: WorkloadConfig(3, "gpt2-medium-sink", 4, 16, 2048, 64, True, 0.125, (0, 1, 2), 1003,
+                      sigma_qk=3.0, kind="sink"),
+    4: WorkloadConfig(4, "llama7b", 1, 32, 8192, 128, True, _inv_sqrt_f32(128), (1, 2), 1004),
+    5: WorkloadConfig(5, "long-tie-grid", 1, 32, 16384, 128, True, _inv_sqrt_f32(128), (1, 2), 1005,
+                      kind="grid"),
+}
+
+
+def _gen(seed: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return g
+
+
+def _randn_bf16(g: torch.Generator, shape, sigma: float = 1.0) -> torch.Tensor:
+    x = torch.randn(shape, generator=g, dtype=torch.float32)
+    if sigma != 1.0:
+        x = x * sigma
+    return x.to(torch.bfloat16)
+
+
+def _grid_bf16(g: torch.Generator, shape) -> torch.Tensor:
+    idx = torch.randint(0, len(GRID_VALUES), shape, generator=g)
+    table = torch.tensor(GRID_VALUES, dtype=torch.float32)
+    return table[idx].to(torch.bfloat16)
+
+
+def randn_inputs(B, H, N, d, seed, sigma_qk=1.0):
+    """Q, K ~ N(0, sigma_qk^2), V, dO ~ N(0, 1); bf16, shape [B, H, N, d]."""
+    g = _gen(seed)
+    shape = (B, H, N, d)
+    q = _randn_bf16(g, shape, sigma_qk)
+    k = _randn_bf16(g, shape, sigma_qk)
+    v = _randn_bf16(g, shape)
+    do = _randn_bf16(g, shape)
+    return {"q": q, "k": k, "v": v, "do": do}
+
+
+def grid_inputs(B, H, N, d, seed):
+    """Q, K uniform over GRID_VALUES (exact ties in row maxima are frequent); V, dO ~ N(0, 1)."""
+    g = _gen(seed)
+    shape = (B, H, N, d)
+    q = _grid_bf16(g, shape)
+    k = _grid_bf16(g, shape)
+    v = _randn_bf16(g, shape)
+    do = _randn_bf16(g, shape)
+    return {"q": q, "k": k, "v": v, "do": do}
+
+
+def _apply_dup(t):
+    """Key 17 := key 3 and queries 0..7 := key 3, so rows 0..7 carry an exact repeated maximum."""
+    k, q = t["k"], t["q"]
+    k[:, :, 17, :] = k[:, :, 3, :]
+    n_rows = min(8, q.shape[2])
+    q[:, :, :n_rows, :] = k[:, :, 3:4, :].expand(-1, -1, n_rows, -1)
+    return t
+
+
+def _apply_sink(t):
+    """Key 0 of each (b, h) := bf16(4 * u), u = the mean query direction normalised to unit length."""
+    q, k = t["q"], t["k"]
+    qm = q.to(torch.float64).mean(dim=2)  # [B, H, d]
+    u = qm / qm.norm(dim=-1, keepdim=True).clamp_min(1e-30)
+    k[:, :, 0, :] = (4.0 * u).to(torch.bfloat16)
+    return t
+
+
+def make_inputs(cfg, **overrides):
+    """Inputs for a workload (a WorkloadConfig or its id); keyword overrides replace B/H/N/d/seed."""
+    if not isinstance(cfg, WorkloadConfig):
+        cfg = CONFIGS[int(cfg)]
+    if overrides:
+        cfg = cfg.with_shape(**overrides)
+    if cfg.kind == "grid":
+        t = grid_inputs(cfg.B, cfg.H, cfg.N, cfg.d, cfg.seed)
+    else:
+        t = randn_inputs(cfg.B, cfg.H, cfg.N, cfg.d, cfg.seed, cfg.sigma_qk)
+    if cfg.kind == "dup":
+        t = _apply_dup(t)
+    elif cfg.kind == "sink":
+        t = _apply_sink(t)
+    return t
+
+
+def tensor_digest(t: torch.Tensor) -> str:
+    """SHA-256 of a tensor's raw bytes (bf16 tensors are hashed through their int16 view)."""
+    if t.dtype == torch.bfloat16:
+        t = t.view(torch.int16)
+    return hashlib.sha256(t.contiguous().numpy().tobytes()).hexdigest()

@@ -1,0 +1,241 @@
+"""Plain fp64 CPU oracle for softmax attention with the stabilised row shift, forward and backward.
+
+TEST INFRASTRUCTURE.  Only the test suite, the package smoke check and the CPU-baseline leg of
+the benchmark may import this module.  The HIP library never calls it, and it shares no code
+with the library.
+
+Every quantity is computed in float64 with numpy, directly from its definition, on the exact
+fp64 images of the bf16 inputs.  Rows are evaluated in chunks only to bound memory: softmax is a
+per-row operation, and the gradient sums over rows are partial sums added in chunk order.
+
+Pages the definitions follow (titles as they appear, sections as numbered there):
+  [FA-practice]  "Flash Attention低精度训练稳定性优化实践" (jsqmd.com/news/761560)
+  [BF16-FA]      the BF16 Flash Attention stability article at ijyty.com/news/896914
+  [FA-backward]  "FlashAttention 训练时为什么会梯度爆炸？一次拆透反向传播的坑" (cnnetsun.cn/a/2497354)
+  [WhyFail]      "為什么BF16的FlashAttention會把訓練「炸掉」？" (web578.cn/c/0305332L962026.html)
+
+Readings where the pages are silent or garbled (the extraction of [BF16-FA] dropped the
+comparison and assignment operators):
+  * the conditional shift of [BF16-FA] §4.1 reads as strict comparisons: rm > 0 and rs > 1
+    give m = beta * rm; rm < 0 and rs > 1 give m = 0; otherwise m = rm;
+  * "mode 2" applies the same rule with the repeat count taken as at least 2, i.e. the shift
+    is applied to every row whether or not a repeat has been seen yet;
+  * causal masking is top-left aligned: key j is visible to query i iff j <= i;
+  * the saved logsumexp uses the natural log of the scaled scores: LSE = m + ln(l).
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+MODE_STANDARD = 0
+MODE_TIE_RULE = 1
+MODE_TIE_ANTICIPATE = 2
+
+
+def bf16_round(x):
+    """Round float64 values to the nearest bfloat16 value, ties to even, returned as float64.
+
+    bfloat16 keeps 8 significant bits (7 stored mantissa bits plus the implicit one) and the fp32
+    exponent range [BF16-FA] §1.  Values are rounded directly from fp64 (no fp32 step).
+    Subnormal and overflow handling is outside what this oracle needs: inputs here are
+    probabilities in [0, 1] and bf16 tensors already.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    mant, expo = np.frexp(x)  # x = mant * 2**expo, |mant| in [0.5, 1)
+    # 8 significant bits: scale the mantissa by 2**8 and round half to even (np.rint is RNE).
+    return np.ldexp(np.rint(np.ldexp(mant, 8)), expo - 8)
+
+
+def visible(rows, n_keys, causal):
+    """Boolean [len(rows), n_keys]: key j is visible to query row i (top-left causal: j <= i)."""
+    rows = np.asarray(rows)
+    keys = np.arange(n_keys)
+    if not causal:
+        return np.ones((rows.size, n_keys), dtype=bool)
+    return keys[None, :] <= rows[:, None]
+
+
+def scaled_scores(q_rows, k, scale, mask):
+    """S = scale * q k^T for a block of query rows; invisible entries are -inf.
+
+    The attention scores of [FA-backward] §3.1 (softmax(QK^T / sqrt(d_k)) V), with the scale
+    passed explicitly.
+    """
+    s = scale * (q_rows @ k.T)
+    return np.where(mask, s, -np.inf)
+
+
+def row_max_and_repeats(s):
+    """rm = rowmax(S) and rs = rowsum(S == rm): the repeated-maximum detection of [BF16-FA] §4.1
+    (the same statistic [BF16-FA] §7.1 suggests monitoring)."""
+    rm = np.max(s, axis=1)
+    rs = np.sum(s == rm[:, None], axis=1).astype(np.int64)
+    return rm, rs
+
+
+def stable_shift(rm, rs, beta, mode):
+    """Row shift m of the safe softmax.
+
+    mode 0: m = rm (the standard safe softmax, [FA-backward] §3.2).
+    mode 1: the conditional shift of [BF16-FA] §4.1 / [WhyFail] mechanism 2: with repeated maxima
+            (rs > 1), m = beta * rm when rm > 0 and m = 0 when rm < 0; otherwise m = rm.
+    mode 2: the same rule with rs replaced by max(rs, 2).
+    """
+    rm = np.asarray(rm, dtype=np.float64)
+    if mode == MODE_STANDARD:
+        return rm.copy()
+    if mode == MODE_TIE_RULE:
+        rep = np.asarray(rs) > 1
+    elif mode == MODE_TIE_ANTICIPATE:
+        rep = np.ones(rm.shape, dtype=bool)
+    else:
+        raise ValueError(f"mode must be 0, 1 or 2, got {mode}")
+    m = np.where((rm > 0) & rep, beta * rm, rm)
+    m = np.where((rm < 0) & rep, 0.0, m)
+    return m
+
+
+@dataclasses.dataclass
+class ForwardResult:
+    o: np.ndarray  # [N, d] normalised output
+    lse: np.ndarray  # [N] natural-log logsumexp of the scaled scores
+    rm: np.ndarray  # [N] row max of the scaled scores
+    rs: np.ndarray  # [N] number of visible keys attaining the row max (int64)
+    m: np.ndarray  # [N] the row shift actually used
+    l: np.ndarray  # [N] sum of the unnormalised probabilities exp(S - m)
+    ones: np.ndarray  # [N] count of bf16(exp(S - m)) == 1.0 over visible keys (int64)
+
+
+def forward(q, k, v, causal, scale, beta=1.25, mode=MODE_STANDARD, row_chunk=1024):
+    """One head of attention: q [N, d], k [N, d], v [N, d] (float64).
+
+    Following the forward of [BF16-FA] §2.1 evaluated without tiling: P_hat = exp(S - m),
+    l = rowsum(P_hat), O = diag(l)^-1 P_hat V, and the logsumexp LSE = m + ln l that the backward
+    uses to rebuild P ([FA-practice] §3.3, [FA-backward] §2).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n, d = q.shape
+    o = np.zeros((n, v.shape[1]))
+    lse = np.zeros(n)
+    rm_all = np.zeros(n)
+    rs_all = np.zeros(n, dtype=np.int64)
+    m_all = np.zeros(n)
+    l_all = np.zeros(n)
+    ones = np.zeros(n, dtype=np.int64)
+    for r0 in range(0, n, row_chunk):
+        rows = np.arange(r0, min(n, r0 + row_chunk))
+        mask = visible(rows, k.shape[0], causal)
+        s = scaled_scores(q[rows], k, scale, mask)
+        rm, rs = row_max_and_repeats(s)
+        m = stable_shift(rm, rs, beta, mode)
+        p_hat = np.exp(s - m[:, None])  # exp(-inf) = 0 on invisible keys
+        l = p_hat.sum(axis=1)
+        o[rows] = (p_hat @ v) / l[:, None]
+        lse[rows] = m + np.log(l)
+        rm_all[rows], rs_all[rows], m_all[rows], l_all[rows] = rm, rs, m, l
+        ones[rows] = np.sum((bf16_round(p_hat) == 1.0) & mask, axis=1)
+    return ForwardResult(o, lse, rm_all, rs_all, m_all, l_all, ones)
+
+
+def probabilities(q_rows, k, scale, lse_rows, mask):
+    """Normalised P = exp(S - LSE) for a block of rows: the recomputation of [FA-backward] §2."""
+    s = scaled_scores(q_rows, k, scale, mask)
+    return np.exp(s - lse_rows[:, None])
+
+
+@dataclasses.dataclass
+class BackwardResult:
+    dq: np.ndarray
+    dk: np.ndarray
+    dv: np.ndarray
+    delta: np.ndarray  # [N] rowsum(dO * O)
+
+
+def backward(q, k, v, do, causal, scale, o=None, lse=None, row_chunk=1024):
+    """Gradients of sum(dO * O) with respect to q, k, v for one head.
+
+    The backward by recomputation of [FA-backward] §2 with the preprocessing term
+    delta = rowsum(dO o O) of [BF16-FA] §3.1.  With P = softmax(S) and S = scale * q k^T:
+      dV = P^T dO,   dP = dO V^T,   dS = P o (dP - delta),
+      dQ = scale * dS K,   dK = scale * dS^T Q.
+    O and LSE are this oracle's own forward results unless given.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    if o is None or lse is None:
+        fr = forward(q, k, v, causal, scale, row_chunk=row_chunk)
+        o, lse = fr.o, fr.lse
+    n = q.shape[0]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    delta = np.sum(do * o, axis=1)
+    for r0 in range(0, n, row_chunk):
+        rows = np.arange(r0, min(n, r0 + row_chunk))
+        mask = visible(rows, k.shape[0], causal)
+        p = probabilities(q[rows], k, scale, lse[rows], mask)
+        dv += p.T @ do[rows]
+        dp = do[rows] @ v.T
+        ds = p * (dp - delta[rows][:, None])
+        dq[rows] = scale * (ds @ k)
+        dk += scale * (ds.T @ q[rows])
+    return BackwardResult(dq, dk, dv, delta)
+
+
+def _heads(x):
+    x = np.asarray(x, dtype=np.float64)
+    if x.ndim != 4:
+        raise ValueError("expected a [B, H, N, d] array")
+    return x
+
+
+def forward_bhnd(q, k, v, causal, scale, beta=1.25, mode=MODE_STANDARD, heads=None, row_chunk=1024):
+    """forward() over [B, H, N, d] arrays.  `heads` restricts the work to a list of (b, h) pairs;
+    the other entries of the outputs stay zero.  Returns a dict of stacked arrays."""
+    q, k, v = _heads(q), _heads(k), _heads(v)
+    B, H, N, d = q.shape
+    out = {
+        "o": np.zeros((B, H, N, v.shape[3])),
+        "lse": np.zeros((B, H, N)),
+        "rm": np.zeros((B, H, N)),
+        "rs": np.zeros((B, H, N), dtype=np.int64),
+        "m": np.zeros((B, H, N)),
+        "l": np.zeros((B, H, N)),
+        "ones": np.zeros((B, H, N), dtype=np.int64),
+    }
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    for b, h in pairs:
+        fr = forward(q[b, h], k[b, h], v[b, h], causal, scale, beta, mode, row_chunk)
+        for name in out:
+            out[name][b, h] = getattr(fr, name)
+    return out
+
+
+def backward_bhnd(q, k, v, do, causal, scale, heads=None, row_chunk=1024):
+    """backward() over [B, H, N, d] arrays, restricted to `heads` if given."""
+    q, k, v, do = _heads(q), _heads(k), _heads(v), _heads(do)
+    B, H, N, d = q.shape
+    out = {name: np.zeros_like(q) for name in ("dq", "dk", "dv")}
+    out["delta"] = np.zeros((B, H, N))
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    for b, h in pairs:
+        br = backward(q[b, h], k[b, h], v[b, h], do[b, h], causal, scale, row_chunk=row_chunk)
+        for name in out:
+            out[name][b, h] = getattr(br, name)
+    return out
+
+
+def flops_forward(B, H, N, d, causal):
+    """The FlashAttention flop convention: 4 B H N^2 d, halved when causal."""
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def exact_causal_pairs(N):
+    return N * (N + 1) // 2

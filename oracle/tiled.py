@@ -1,0 +1,106 @@
+"""fp64 replay of the tiled online-softmax forward, with the per-tile stabilised shift.
+
+TEST INFRASTRUCTURE.  Only the test suite, the package smoke check and the CPU-baseline leg of
+the benchmark may import this module; the HIP library never calls it.
+
+It follows the online softmax of the BF16 Flash Attention article at ijyty.com/news/896914, §2.1,
+step by step over key blocks of width `bc` (all query rows at once, in float64):
+
+    m   = shift(running max, running repeat count)
+    P^  = exp(S - m)
+    l   = exp(m_prev - m) * l_prev + rowsum(P^)
+    O   = diag(exp(m_prev - m)) O_prev + P^ V
+and at the end O = diag(l)^-1 O, LSE = m + ln l.
+
+The pages do not say how repeated maxima are counted across blocks.  The reading taken here:
+the block maximum tm and its count tc are merged into a running (r, c) by
+    r' = max(r, tm),   c' = [tm == r'] tc + [r == r'] c,
+so after the last block c equals the untiled count, and the shift of §4.1 is applied per block
+from the running (r, c).  With the tie-conditional rule (mode 1) the first occurrence of a
+maximum whose repeat only arrives in a later block is exponentiated with m = r and gives an
+unnormalised probability of exactly 1.0; the `ones` output counts those, per row, exactly as a
+kernel that processes key blocks in the same order and width would produce them.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import bf16_round, stable_shift, visible
+
+
+def tiled_forward(q, k, v, causal, scale, beta=1.25, mode=0, bc=64, order=None):
+    """Tiled forward over one head; returns dict(o, lse, r, c, m, ones).
+
+    `order` lists the key-block indices in processing order (default: ascending).  Key blocks
+    entirely invisible to a row leave that row's state unchanged.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n = q.shape[0]
+    n_keys = k.shape[0]
+    n_blocks = -(-n_keys // bc)
+    if order is None:
+        order = range(n_blocks)
+    rows = np.arange(n)
+    mask_all = visible(rows, n_keys, causal)
+
+    r = np.full(n, -np.inf)
+    c = np.zeros(n, dtype=np.int64)
+    m = np.full(n, -np.inf)
+    l = np.zeros(n)
+    acc = np.zeros((n, v.shape[1]))
+    ones = np.zeros(n, dtype=np.int64)
+    for j in order:
+        k0, k1 = j * bc, min(n_keys, (j + 1) * bc)
+        mask = mask_all[:, k0:k1]
+        s = np.where(mask, scale * (q @ k[k0:k1].T), -np.inf)
+        tm = np.max(s, axis=1)
+        tc = np.sum((s == tm[:, None]) & mask, axis=1)
+        r_new = np.maximum(r, tm)
+        c = np.where(tm == r_new, tc, 0) + np.where(r == r_new, c, 0)
+        r = r_new
+        live = np.isfinite(r)  # rows that have seen at least one visible key
+        m_new = np.where(live, stable_shift(np.where(live, r, 0.0), c, beta, mode), -np.inf)
+        alpha = np.where(np.isfinite(m), np.exp(np.where(np.isfinite(m), m, 0.0) - np.where(live, m_new, 0.0)), 0.0)
+        p_hat = np.where(mask, np.exp(s - np.where(live, m_new, 0.0)[:, None]), 0.0)
+        l = alpha * l + p_hat.sum(axis=1)
+        acc = alpha[:, None] * acc + p_hat @ v[k0:k1]
+        ones += np.sum((bf16_round(p_hat) == 1.0) & mask, axis=1)
+        m = m_new
+    o = acc / l[:, None]
+    lse = m + np.log(l)
+    return {"o": o, "lse": lse, "r": r, "c": c, "m": m, "ones": ones}
+
+
+def tiled_ones(q, k, causal, scale, beta=1.25, mode=0, bc=64, order=None):
+    """Per-row count of exact-1.0 bf16 unnormalised probabilities under block-wise processing.
+
+    Same recurrence as tiled_forward without V; used where only the count is needed (large
+    heads), to save the P^ V product.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    n = q.shape[0]
+    n_keys = k.shape[0]
+    n_blocks = -(-n_keys // bc)
+    if order is None:
+        order = range(n_blocks)
+    rows = np.arange(n)
+    r = np.full(n, -np.inf)
+    c = np.zeros(n, dtype=np.int64)
+    ones = np.zeros(n, dtype=np.int64)
+    for j in order:
+        k0, k1 = j * bc, min(n_keys, (j + 1) * bc)
+        mask = visible(rows, n_keys, causal)[:, k0:k1]
+        s = np.where(mask, scale * (q @ k[k0:k1].T), -np.inf)
+        tm = np.max(s, axis=1)
+        tc = np.sum((s == tm[:, None]) & mask, axis=1)
+        r_new = np.maximum(r, tm)
+        c = np.where(tm == r_new, tc, 0) + np.where(r == r_new, c, 0)
+        r = r_new
+        live = np.isfinite(r)
+        m = stable_shift(np.where(live, r, 0.0), c, beta, mode)
+        p_hat = np.where(mask, np.exp(s - m[:, None]), 0.0)
+        ones += np.sum((bf16_round(p_hat) == 1.0) & mask, axis=1)
+    return ones

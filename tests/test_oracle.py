@@ -1,0 +1,469 @@
+"""Pins for the fp64 oracle: each check ties it to something other than its own code.
+
+Pins used: brute force with scalar Python loops, the pages' printed numbers and closed forms,
+torch's bf16 cast, finite differences, exact integer arithmetic, and invariants of the gradient.
+None of these tests touches a GPU.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from inputs import make_inputs, grid_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+BETA = 1.25
+
+
+def _np(t):
+    return t.to(torch.float64).numpy()
+
+
+def _head(t, b=0, h=0):
+    return {k: _np(v[b, h]) for k, v in t.items()}
+
+
+def _scores_row(values, scale=1.0):
+    """Q and K with one query row whose scaled scores are exactly `values` (d = 2)."""
+    n = len(values)
+    q = np.zeros((1, 2))
+    q[0, 0] = 1.0
+    k = np.zeros((n, 2))
+    k[:, 0] = np.asarray(values, dtype=np.float64) / scale
+    return q, k
+
+
+# ----------------------------------------------------------------------------------------------
+# bf16 rounding (the format of the BF16 article, §1; RNE per its §2.2)
+
+
+def test_bf16_round_matches_torch_cast():
+    rng = np.random.default_rng(7)
+    x = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        rng.uniform(0.98, 1.0, 20000).astype(np.float32),
+        np.exp(-rng.uniform(0, 30, 20000)).astype(np.float32),
+    ])
+    # exact halfway cases between adjacent bf16 values, both parities
+    base = np.array([1.0, 1.0078125, 0.99609375, 3.0, 0.5], dtype=np.float32)
+    ulp = np.array([2 ** -7, 2 ** -7, 2 ** -8, 2 ** -6, 2 ** -9], dtype=np.float32)
+    x = np.concatenate([x, base + ulp / 2, base - ulp / 4 * 0 - ulp / 2])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.bf16_round(x.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+def test_bf16_round_threshold_below_one():
+    # the largest value below 1 that still rounds to 1.0: 1 - 2^-9 (a tie, rounds to even = 1.0)
+    assert oracle.bf16_round(1 - 2 ** -9) == 1.0
+    assert oracle.bf16_round(np.nextafter(1 - 2 ** -9, 0)) == 1 - 2 ** -8
+
+
+def test_pages_printed_numbers():
+    g = json.load(open(os.path.join(GOLDEN, "pages_numbers.json")))
+    assert np.float16(g["fp16_max"]["value"]) == np.finfo(np.float16).max
+    assert abs(float(np.finfo(np.float16).smallest_subnormal) - g["fp16_min_positive"]["value"]) < 1e-9
+    for key in ("exp_11", "exp_12"):
+        x = 11.0 if key == "exp_11" else 12.0
+        assert abs(math.exp(x) - g[key]["value"]) < 1.0  # the page prints the value truncated
+        assert np.isfinite(np.float16(math.exp(x))) == g[key]["fits_fp16"]
+    # bf16: 8 exponent bits, 7 stored mantissa bits => spacing just above 1 is 2^-7
+    assert g["bf16_mantissa_bits"]["value"] == 7
+    assert oracle.bf16_round(1 + 2 ** -8 + 2 ** -10) == 1 + 2 ** -7
+    assert float(torch.finfo(torch.bfloat16).max) > 3e38  # fp32's exponent range (8 bits)
+    assert g["beta_range"]["value"][0] <= g["beta_default"]["value"] <= g["beta_range"]["value"][1]
+
+
+# ----------------------------------------------------------------------------------------------
+# P1: brute force, scalar Python loops, no shift at all
+
+
+def _brute_force(q, k, v, causal, scale):
+    n, d = len(q), len(q[0])
+    o = [[0.0] * len(v[0]) for _ in range(n)]
+    lse = [0.0] * n
+    for i in range(n):
+        keys = [j for j in range(len(k)) if (not causal or j <= i)]
+        e = {}
+        for j in keys:
+            s = 0.0
+            for c in range(d):
+                s += q[i][c] * k[j][c]
+            e[j] = math.exp(scale * s)
+        z = sum(e.values())
+        lse[i] = math.log(z)
+        for c in range(len(v[0])):
+            o[i][c] = sum(e[j] * v[j][c] for j in keys) / z
+    return np.array(o), np.array(lse)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_brute_force_tiny(causal, mode):
+    rng = np.random.default_rng(11 + mode)
+    for n, d in [(1, 3), (5, 4), (16, 8)]:
+        q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+        if n > 3:
+            k[3] = k[1]  # a repeated key
+            q[2] = k[1]
+        o_ref, lse_ref = _brute_force(q.tolist(), k.tolist(), v.tolist(), causal, 0.7)
+        fr = oracle.forward(q, k, v, causal, 0.7, BETA, mode)
+        np.testing.assert_allclose(fr.o, o_ref, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(fr.lse, lse_ref, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------------------------
+# P2, P3: normalisation and shift invariance
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_rows_sum_to_one(causal):
+    t = _head(make_inputs(3, B=1, H=1, N=256))
+    fr = oracle.forward(t["q"], t["k"], t["v"], causal, 0.125)
+    rows = np.arange(256)
+    p = oracle.probabilities(t["q"], t["k"], 0.125, fr.lse, oracle.visible(rows, 256, causal))
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    assert np.all(p[~oracle.visible(rows, 256, causal)] == 0)
+
+
+@pytest.mark.parametrize("kind", ["grid", "sink", "dup"])
+def test_shift_cancels_between_modes(kind):
+    cid = {"grid": 5, "sink": 3, "dup": 1}[kind]
+    t = _head(make_inputs(cid, B=1, H=1, N=128, d=64))
+    outs = [oracle.forward(t["q"], t["k"], t["v"], True, 0.125, BETA, mode) for mode in (0, 1, 2)]
+    for fr in outs[1:]:
+        np.testing.assert_allclose(fr.o, outs[0].o, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(fr.lse, outs[0].lse, rtol=1e-12, atol=1e-12)
+    # the shift is really different where it should be
+    assert np.any(outs[2].m != outs[0].m)
+
+
+# ----------------------------------------------------------------------------------------------
+# P4: tiled recurrence == untiled definition
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("bc", [1, 7, 32, 64, 200])
+def test_tiled_recurrence_matches_untiled(causal, mode, bc):
+    t = _head(grid_inputs(1, 1, 200, 16, seed=5))
+    fr = oracle.forward(t["q"], t["k"], t["v"], causal, 0.3, BETA, mode)
+    tr = oracle.tiled_forward(t["q"], t["k"], t["v"], causal, 0.3, BETA, mode, bc=bc)
+    np.testing.assert_allclose(tr["o"], fr.o, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(tr["lse"], fr.lse, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(tr["c"], fr.rs)
+    assert np.array_equal(tr["r"], fr.rm)
+
+
+def test_tiled_order_does_not_change_result():
+    t = _head(make_inputs(3, B=1, H=1, N=192))
+    a = oracle.tiled_forward(t["q"], t["k"], t["v"], False, 0.125, BETA, 1, bc=64)
+    b = oracle.tiled_forward(t["q"], t["k"], t["v"], False, 0.125, BETA, 1, bc=64, order=[2, 0, 1])
+    np.testing.assert_allclose(a["o"], b["o"], rtol=1e-12, atol=1e-12)
+    assert np.array_equal(a["c"], b["c"])
+
+
+# ----------------------------------------------------------------------------------------------
+# P5: finite differences of L = sum(dO * O)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("ties", [False, True])
+def test_gradients_match_finite_differences(causal, ties):
+    rng = np.random.default_rng(3 + 2 * causal + ties)
+    n, d, scale = 8, 8, 0.5
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    if ties:
+        k[5] = k[2]
+        q[6] = k[2]
+    br = oracle.backward(q, k, v, do, causal, scale)
+
+    def loss(qq, kk, vv):
+        return float(np.sum(do * oracle.forward(qq, kk, vv, causal, scale).o))
+
+    h = 1e-6
+    for name, grad in (("q", br.dq), ("k", br.dk), ("v", br.dv)):
+        fd = np.zeros((n, d))
+        for i in range(n):
+            for c in range(d):
+                args = {"q": q.copy(), "k": k.copy(), "v": v.copy()}
+                args[name][i, c] += h
+                lp = loss(args["q"], args["k"], args["v"])
+                args[name][i, c] -= 2 * h
+                lm = loss(args["q"], args["k"], args["v"])
+                fd[i, c] = (lp - lm) / (2 * h)
+        scale_ref = max(1.0, np.abs(grad).max())
+        np.testing.assert_allclose(grad, fd, rtol=1e-6, atol=1e-6 * scale_ref, err_msg=name)
+
+
+# ----------------------------------------------------------------------------------------------
+# P6: closed forms
+
+
+def test_closed_forms_causal_row0_constant_v_zero_q():
+    rng = np.random.default_rng(21)
+    n, d, scale = 64, 16, 0.25
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    fr = oracle.forward(q, k, v, True, scale)
+    np.testing.assert_allclose(fr.o[0], v[0], rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(fr.lse[0], scale * q[0] @ k[0], rtol=1e-14, atol=1e-14)
+    br = oracle.backward(q, k, v, do, True, scale)
+    np.testing.assert_allclose(br.dq[0], 0.0, atol=1e-14)
+
+    vc = np.tile(rng.standard_normal(d), (n, 1))
+    for causal in (False, True):
+        fr = oracle.forward(q, k, vc, causal, scale)
+        np.testing.assert_allclose(fr.o, vc, rtol=1e-13, atol=1e-13)
+
+    q0 = np.zeros((n, d))
+    for causal in (False, True):
+        fr = oracle.forward(q0, k, v, causal, scale)
+        cnt = np.arange(1, n + 1) if causal else np.full(n, n)
+        mean = np.cumsum(v, axis=0) / cnt[:, None] if causal else np.tile(v.mean(axis=0), (n, 1))
+        np.testing.assert_allclose(fr.o, mean, rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(fr.lse, np.log(cnt), rtol=1e-14, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------------------------
+# P7: the tie closed form of the BF16 article §3.2 (k equal maxima)
+
+
+@pytest.mark.parametrize("n_ties", [2, 3, 5])
+@pytest.mark.parametrize("s_max", [2.0, 0.75, -1.5])
+def test_tie_closed_form(n_ties, s_max):
+    others = [s_max - 9.0, s_max - 11.5, s_max - 30.0]
+    values = [s_max] * n_ties + others
+    q, k = _scores_row(values)
+    v = np.eye(len(values))  # O = P, so the output row is the probability row
+    tail = sum(math.exp(x - s_max) for x in others)
+    for mode in (0, 1, 2):
+        fr = oracle.forward(q, k, v, False, 1.0, BETA, mode)
+        # normalised probability at each tied maximum: 1 / (k + tail), in every mode
+        np.testing.assert_allclose(fr.o[0, :n_ties], 1.0 / (n_ties + tail), rtol=1e-13)
+        assert fr.rs[0] == n_ties
+        p_hat_max = math.exp(s_max - fr.m[0])
+        if mode == 0:
+            assert fr.m[0] == s_max and p_hat_max == 1.0 and fr.ones[0] == n_ties
+        elif s_max > 0:
+            # stabilised: P^ at the max = exp(-(beta - 1) * s_max) < 1
+            assert fr.m[0] == BETA * s_max
+            assert abs(p_hat_max - math.exp(-(BETA - 1) * s_max)) < 1e-15
+            assert fr.ones[0] == 0
+        else:
+            # negative maximum: m = 0, P^ = exp(s_max)
+            assert fr.m[0] == 0.0
+            assert abs(p_hat_max - math.exp(s_max)) < 1e-15
+            assert fr.ones[0] == 0
+
+
+def test_shift_rule_without_repeats():
+    q, k = _scores_row([2.0, 1.0, -3.0])
+    v = np.eye(3)
+    assert oracle.forward(q, k, v, False, 1.0, BETA, 1).m[0] == 2.0  # unique max: no shift
+    assert oracle.forward(q, k, v, False, 1.0, BETA, 2).m[0] == 2.5  # anticipating rule shifts
+    q, k = _scores_row([0.0, 0.0, -3.0])  # rm == 0 with a repeat: no branch fires
+    fr = oracle.forward(q, k, np.eye(3), False, 1.0, BETA, 1)
+    assert fr.m[0] == 0.0 and fr.ones[0] == 2
+
+
+# ----------------------------------------------------------------------------------------------
+# P8: repeat counts by exact integer arithmetic on grid inputs
+
+
+def test_dupcount_by_integer_arithmetic():
+    t = grid_inputs(1, 2, 384, 64, seed=99)
+    for h in range(2):
+        q = t["q"][0, h].to(torch.float64).numpy()
+        k = t["k"][0, h].to(torch.float64).numpy()
+        qi = np.rint(2 * q).astype(np.int64)  # grid entries are multiples of 0.5
+        ki = np.rint(2 * k).astype(np.int64)
+        x4 = qi @ ki.T  # 4 * (q . k), exact
+        for causal in (False, True):
+            mask = oracle.visible(np.arange(384), 384, causal)
+            xm = np.where(mask, x4, np.iinfo(np.int64).min)
+            mx = xm.max(axis=1)
+            rs = np.sum(xm == mx[:, None], axis=1)
+            fr = oracle.forward(q, k, q, causal, 0.0883883461356163, BETA, 1)
+            assert np.array_equal(fr.rs, rs)
+            assert rs.max() > 1  # the grid really produces ties
+
+
+def test_dupcount_config1_construction():
+    t = _head(make_inputs(1))
+    fr = oracle.forward(t["q"], t["k"], t["v"], False, 0.125, BETA, 0)
+    assert np.all(fr.rs[:8] == 2)
+    # any other row whose maximum falls on key 3 (= key 17) repeats too; all the rest are unique
+    s = 0.125 * t["q"] @ t["k"].T
+    on_dup = np.isin(np.argmax(s, axis=1), [3, 17])
+    assert np.array_equal(fr.rs, np.where(on_dup, 2, 1))
+    top2 = np.sort(0.125 * t["q"][:8] @ t["k"].T, axis=1)[:, -3:]
+    assert np.all(top2[:, -1] == top2[:, -2])
+    assert np.all(top2[:, -2] - top2[:, -3] > 1.0)
+
+
+# ----------------------------------------------------------------------------------------------
+# P9: gradient invariants
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gradient_invariants(causal):
+    t = _head(make_inputs(2, B=1, H=1, N=256))
+    scale = 0.125
+    fr = oracle.forward(t["q"], t["k"], t["v"], causal, scale)
+    br = oracle.backward(t["q"], t["k"], t["v"], t["do"], causal, scale)
+    rows = np.arange(256)
+    mask = oracle.visible(rows, 256, causal)
+    p = oracle.probabilities(t["q"], t["k"], scale, fr.lse, mask)
+    dp = t["do"] @ t["v"].T
+    np.testing.assert_allclose(br.delta, np.sum(p * dp, axis=1), rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(br.dk.sum(axis=0), 0.0, atol=1e-10)
+    np.testing.assert_allclose(br.dv.sum(axis=0), t["do"].sum(axis=0), rtol=1e-11, atol=1e-10)
+    np.testing.assert_allclose(np.sum(t["q"] * br.dq), np.sum(t["k"] * br.dk), rtol=1e-10, atol=1e-10)
+
+
+# ----------------------------------------------------------------------------------------------
+# P11: tile replay of the exact-1.0 count vs a scalar per-tile replay
+
+
+def _scalar_tile_ones(q, k, causal, scale, beta, mode, bc):
+    n = len(q)
+    out = []
+    for i in range(n):
+        r, c, ones = -math.inf, 0, 0
+        for j0 in range(0, len(k), bc):
+            keys = [j for j in range(j0, min(len(k), j0 + bc)) if (not causal or j <= i)]
+            if not keys:
+                continue
+            s = {j: scale * float(np.dot(q[i], k[j])) for j in keys}
+            tm = max(s.values())
+            tc = sum(1 for x in s.values() if x == tm)
+            rn = max(r, tm)
+            c = (tc if tm == rn else 0) + (c if r == rn else 0)
+            r = rn
+            rep = c > 1 if mode == 1 else (mode == 2)
+            m = beta * r if (r > 0 and rep) else (0.0 if (r < 0 and rep) else r)
+            for x in s.values():
+                if oracle.bf16_round(math.exp(x - m)) == 1.0:
+                    ones += 1
+        out.append(ones)
+    return np.array(out)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_tile_ones_vs_scalar_replay(causal, mode):
+    t = _head(grid_inputs(1, 1, 48, 8, seed=17))
+    scale = 0.35
+    want = _scalar_tile_ones(t["q"], t["k"], causal, scale, BETA, mode, 16)
+    got = oracle.tiled_ones(t["q"], t["k"], causal, scale, BETA, mode, bc=16)
+    got2 = oracle.tiled_forward(t["q"], t["k"], t["v"], causal, scale, BETA, mode, bc=16)["ones"]
+    assert np.array_equal(got, want)
+    assert np.array_equal(got2, want)
+
+
+def test_mode1_residual_and_mode2_zero():
+    # max 2.0 at key 1 (block 0) repeated at key 5 (block 1) with bc = 4: mode 1 emits one exact
+    # 1.0 (at key 1, before the repeat is seen); mode 2 and the untiled rule emit none.
+    q, k = _scores_row([0.5, 2.0, -1.0, 0.25, 1.0, 2.0, -2.0, 0.0])
+    v = np.eye(8)
+    assert oracle.tiled_forward(q, k, v, False, 1.0, BETA, 1, bc=4)["ones"][0] == 1
+    assert oracle.tiled_forward(q, k, v, False, 1.0, BETA, 2, bc=4)["ones"][0] == 0
+    assert oracle.forward(q, k, v, False, 1.0, BETA, 1).ones[0] == 0
+    assert oracle.tiled_forward(q, k, v, False, 1.0, BETA, 1, bc=8)["ones"][0] == 0
+
+
+def test_mode2_no_ones_on_grid_away_from_zero():
+    t = _head(grid_inputs(1, 1, 512, 128, seed=5))
+    scale = 0.0883883461356163
+    fr = oracle.forward(t["q"], t["k"], t["v"], True, scale, BETA, 0)
+    ones = oracle.tiled_ones(t["q"], t["k"], True, scale, BETA, 2, bc=64)
+    away = fr.rm != 0
+    assert np.all(ones[away] == 0)
+    ones1 = oracle.tiled_ones(t["q"], t["k"], True, scale, BETA, 1, bc=64)
+    assert ones1[away].sum() > 0  # the tie-conditional rule leaves some, as predicted
+
+
+# ----------------------------------------------------------------------------------------------
+# Planted mistakes: the pins above must reject a plausibly wrong oracle.  Each mutation is built
+# here, on the CPU, from the oracle's own pieces with one term changed.
+
+
+def _fd_gradient_error(backward_fn, causal=True):
+    rng = np.random.default_rng(5)
+    n, d, scale = 8, 8, 0.5
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    grads = backward_fn(q, k, v, do, causal, scale)
+    worst = 0.0
+    h = 1e-6
+    for idx, (name, base) in enumerate((("q", q), ("k", k), ("v", v))):
+        for i in range(n):
+            for c in range(d):
+                args = [q.copy(), k.copy(), v.copy()]
+                args[idx][i, c] += h
+                lp = np.sum(do * oracle.forward(*args, causal, scale).o)
+                args[idx][i, c] -= 2 * h
+                lm = np.sum(do * oracle.forward(*args, causal, scale).o)
+                worst = max(worst, abs(grads[idx][i, c] - (lp - lm) / (2 * h)))
+    return worst
+
+
+def _backward_variant(q, k, v, do, causal, scale, flaw):
+    fr = oracle.forward(q, k, v, causal, scale)
+    n = len(q)
+    mask = oracle.visible(np.arange(n), n, causal)
+    p = oracle.probabilities(q, k, scale, fr.lse, mask)
+    delta = np.sum(do * fr.o, axis=1)
+    if flaw == "delta_sign":
+        delta = -delta
+    dv = p.T @ do
+    dp = do @ v.T
+    ds = p * (dp - delta[:, None])
+    if flaw == "drop_delta":
+        ds = p * dp
+    dq = scale * ds @ k
+    dk = scale * ds.T @ q
+    if flaw == "transposed_dk":
+        dk = scale * ds @ q
+    if flaw == "missing_scale":
+        dq = ds @ k
+    return dq, dk, dv
+
+
+def test_planted_gradient_mistakes_are_caught():
+    good = _fd_gradient_error(lambda *a: _backward_variant(*a, flaw=None))
+    assert good < 1e-6
+    for flaw in ("delta_sign", "drop_delta", "transposed_dk", "missing_scale"):
+        assert _fd_gradient_error(lambda *a: _backward_variant(*a, flaw=flaw)) > 1e-3, flaw
+
+
+def test_planted_shift_mistakes_are_caught():
+    # a shift that forgets beta, or shifts negative maxima by beta, breaks the tie closed form
+    rm = np.array([2.0, -1.5])
+    rs = np.array([3, 3])
+    good = oracle.stable_shift(rm, rs, BETA, 1)
+    assert good[0] == BETA * 2.0 and good[1] == 0.0
+    forgot_beta = np.where((rm > 0) & (rs > 1), 1.0 * rm, rm)
+    assert math.exp(2.0 - forgot_beta[0]) == 1.0  # the exact 1.0 the rule exists to avoid
+    wrong_neg = np.where(rs > 1, BETA * rm, rm)
+    assert math.exp(-1.5 - wrong_neg[1]) > 1.0  # P^ above 1 for a negative maximum
+
+
+def test_planted_count_merge_mistake_is_caught():
+    # merging tile counts without checking which maximum survives over-counts repeats
+    t = _head(grid_inputs(1, 1, 128, 16, seed=3))
+    good = oracle.tiled_forward(t["q"], t["k"], t["v"], False, 0.3, BETA, 1, bc=16)["c"]
+    s = 0.3 * t["q"] @ t["k"].T
+    r = np.full(128, -np.inf)
+    c = np.zeros(128, dtype=np.int64)
+    for j0 in range(0, 128, 16):
+        blk = s[:, j0:j0 + 16]
+        tm = blk.max(axis=1)
+        tc = np.sum(blk == tm[:, None], axis=1)
+        c = c + tc  # the planted mistake: counts of smaller maxima leak in
+        r = np.maximum(r, tm)
+    assert np.array_equal(good, oracle.forward(t["q"], t["k"], t["v"], False, 0.3, BETA, 1).rs)
+    assert not np.array_equal(c, good)
