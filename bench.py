@@ -1,0 +1,201 @@
+"""Benchmark: stabilised BF16 attention forward + backward on one MI355X.
+
+One step = one forward (fa_fwd) and one backward (fa_bwd) over a fixed synthetic batch already
+resident in HBM.  Default workload: the LLaMA-7B-shaped attention layer (B=1, H=32, N=8192,
+d=128, causal, scale 1/sqrt(128)), tie-conditional stabilised shift (stable_flag=1, beta=1.25).
+
+Throughput uses the FlashAttention flop convention: forward 4*B*H*N^2*d (halved when causal),
+backward 2.5x the forward.  Per-kernel durations are measured with HIP events on the stream the
+kernels are launched on.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s fwd & fwd+bwd (bf16, % MFMA peak), N=8192 d=128 causal"
+# MI355X published peaks: dense bf16 MFMA and HBM3E bandwidth.
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+
+
+def fwd_flops(B, H, N, d, causal):
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=4, help="workload id (1-5)")
+    ap.add_argument("--mode", type=int, default=1, help="stable_flag: 0, 1 or 2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-iters", type=int, default=20)
+    return ap.parse_args()
+
+
+def time_events(fn, iters, stream):
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(iters):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / iters  # ms
+
+
+def cpu_baseline(cfg, t, mode):
+    """The fp64 oracle, as it stands, on one head of the workload (forward + backward)."""
+    import numpy as np
+    import torch
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing or no BLAS pool reported
+        threads = os.cpu_count() or 1
+    x = {k: v[0, 0].to(torch.float64).numpy() for k, v in t.items()}
+    t0 = time.perf_counter()
+    fr = oracle.forward(x["q"], x["k"], x["v"], cfg.causal, cfg.scale, 1.25, mode)
+    oracle.backward(x["q"], x["k"], x["v"], x["do"], cfg.causal, cfg.scale, o=fr.o, lse=fr.lse)
+    dt = time.perf_counter() - t0
+    flops = 3.5 * fwd_flops(1, 1, cfg.N, cfg.d, cfg.causal)
+    assert np.isfinite(fr.o).all()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"1 of {cfg.B * cfg.H} heads (b=0,h=0), forward+backward, fp64 numpy, "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the attention heads of this "
+              "workload shard across GPUs without communication, and this build measures the "
+              "one-GPU kernel.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import precision_numerical_stability_amd as fa
+    from inputs import CONFIGS, make_inputs, tensor_digest
+
+    cfg = CONFIGS[args.config]
+    B, H, N, d = cfg.B, cfg.H, cfg.N, cfg.d
+    t = make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    g = {k: v.to(dev) for k, v in t.items()}
+    q, k, v, do = g["q"], g["k"], g["v"], g["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    causal, scale, mode = cfg.causal, cfg.scale, args.mode
+
+    def run_fwd():
+        fa.fa_fwd(q, k, v, o, lse, causal, scale, 1.25, mode, stream=stream)
+
+    def run_stage(stages):
+        return lambda: fa.fa_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, delta, causal, scale,
+                                    stages=stages, stream=stream)
+
+    def step():
+        run_fwd()
+        fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, causal, scale, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+
+    # Per-kernel durations (separate loops, same stream, after the timed region).
+    it = args.kernel_iters
+    ms_fwd = time_events(run_fwd, it, stream)
+    ms_delta = time_events(run_stage(fa.FA_BWD_DELTA), it, stream)
+    ms_dkdv = time_events(run_stage(fa.FA_BWD_DKDV), it, stream)
+    ms_dq = time_events(run_stage(fa.FA_BWD_DQ), it, stream)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(dq.float()).all()
+
+    ff = fwd_flops(B, H, N, d, causal)
+    total = 3.5 * ff
+    value = total / (ms_step * 1e-3) / 1e12
+    fwd_tf = ff / (ms_fwd * 1e-3) / 1e12
+    pairs = B * H * (N * (N + 1) // 2 if causal else N * N)
+    # Algorithmic work per kernel: forward 4d flop per visible pair (two contractions); the dK/dV
+    # kernel 8d (S recompute, dP, dV, dK); the dQ kernel 2d (dQ; its S and dP recomputes are
+    # extra work); delta reads O and dO and writes one fp32 per row.
+    alg = {
+        "fwd": ("mfma", ff, ms_fwd),
+        "dkdv": ("mfma", 2.0 * ff, ms_dkdv),
+        "dq": ("mfma", 0.5 * ff, ms_dq),
+        "delta": ("hbm", 2.0 * B * H * N * d * 2 + B * H * N * 4, ms_delta),
+    }
+    ms_by_kernel = {"fwd": ms_fwd, "delta": ms_delta, "dkdv": ms_dkdv, "dq": ms_dq}
+    dom = max(ms_by_kernel, key=ms_by_kernel.get)
+    bound, work, ms = alg[dom]
+    if bound == "mfma":
+        achieved = work / (ms * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None}
+    else:
+        achieved = work / (ms * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None}
+    kernels = {}
+    for name, (bnd, work_k, ms_k) in alg.items():
+        if bnd == "mfma":
+            tf = work_k / (ms_k * 1e-3) / 1e12
+            kernels[name] = {"ms": ms_k, "TFLOP/s": tf, "frac_bf16_peak": tf / PEAK_BF16_TFLOPS}
+        else:
+            gbs = work_k / (ms_k * 1e-3) / 1e9
+            kernels[name] = {"ms": ms_k, "GB/s": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS}
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} attention layer", "B": B, "H": H, "N": N, "d": d,
+                   "causal": causal, "scale": scale, "stable_flag": mode, "beta": 1.25,
+                   "seed": cfg.seed, "q_sha256": tensor_digest(t["q"])[:16]},
+        "fwd_tflops": fwd_tf,
+        "fwd_frac_peak": fwd_tf / PEAK_BF16_TFLOPS,
+        "fwdbwd_tflops": value,
+        "fwdbwd_frac_peak": value / PEAK_BF16_TFLOPS,
+        "exact_causal_pairs": pairs,
+        "kernels": kernels,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, t, mode)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

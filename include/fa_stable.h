@@ -1,0 +1,129 @@
+/*
+ * fa_stable.h -- C ABI of a BF16 FlashAttention forward/backward library for AMD MI355X (gfx950),
+ * with the stabilised safe-softmax shift for repeated row maxima.
+ *
+ * Operations (pages cited by title/address and section):
+ *   - forward: the tiled online softmax of the BF16 Flash Attention article
+ *     (ijyty.com/news/896914) §2.1 -- S = scale * Q K^T per block, running max m and running sum l,
+ *     P^ = exp(S - m), O accumulated as diag(exp(m_prev - m)) O + P^ V, final O = diag(l)^-1 O --
+ *     with the mixed-precision schedule of "Flash Attention低精度训练稳定性优化实践"
+ *     (jsqmd.com/news/761560) §3.2 (fp32 accumulation of Q K^T, fp32 softmax, bf16 P^ V product)
+ *     and the saved logsumexp of its §3.3;
+ *   - stabilised shift: the repeated-maximum detection and conditional shift of the same article
+ *     §4.1 (and "為什么BF16的FlashAttention會把訓練「炸掉」？", web578.cn, mechanism 2): with a
+ *     repeated row maximum rm, m = beta * rm when rm > 0 and m = 0 when rm < 0;
+ *   - backward: recomputation of P from the saved logsumexp ("FlashAttention 训练时为什么会梯度爆炸",
+ *     cnnetsun.cn/a/2497354, §2), delta = rowsum(dO o O) (ijyty.com article §3.1), then dQ, dK, dV.
+ *
+ * Conventions shared by every entry point:
+ *   - q, k, v, o, dO, dq, dk, dv: device pointers to contiguous [B, H, N, d] bfloat16 tensors
+ *     (row-major, d fastest), 16-byte aligned.  bfloat16 is passed as raw 16-bit storage.
+ *   - lse, delta workspace: device pointers to contiguous [B, H, N] float32, 4-byte aligned.
+ *     lse holds the natural-log logsumexp of the scaled scores: LSE = m + ln(l).
+ *   - dupcnt, ones: device pointers to contiguous [B, H, N] int32, 4-byte aligned.
+ *   - B, H, N >= 0 (an empty problem, B*H*N == 0, is a successful no-op); d is 64 or 128.
+ *     N need not be a multiple of any tile size.  B*H*N*d < 2^40.
+ *   - causal: 0 or 1; causal masking is top-left aligned (key j is visible to query i iff j <= i).
+ *   - scale: the score scale (typically 1/sqrt(d)), finite and > 0.
+ *   - beta: the shift factor for positive repeated maxima, finite and >= 1 (1.25 recommended by
+ *     the ijyty.com article §3.2).
+ *   - stable_flag: 0 = standard safe softmax (m = running max);
+ *                  1 = the pages' tie-conditional rule, applied per key block from the running
+ *                      (max, repeat count) merged across blocks;
+ *                  2 = tie-anticipating rule: the same shift applied whether or not a repeat has
+ *                      been seen yet, so no unnormalised probability at a positive or negative
+ *                      maximum can round to exactly 1.0.
+ *     O, LSE and the gradients do not depend on stable_flag (the shift cancels on normalising).
+ *   - stream: a hipStream_t (NULL = the default stream).  Every call is asynchronous on it.
+ *
+ * Ownership and behaviour: the caller allocates every buffer; the library never allocates, frees
+ * or synchronises, keeps no per-call state and may be called from several threads.  Outputs are
+ * overwritten, never accumulated into.  Every argument is validated before any HIP call; invalid
+ * arguments return an error status and launch nothing.  A HIP failure returns FA_ERR_HIP and the
+ * raw hipError_t value is available from fa_last_hip_error() on the calling thread.  Nothing is
+ * thrown across the ABI.
+ */
+#ifndef FA_STABLE_H
+#define FA_STABLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,    /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,   /* B, H or N negative, or the problem too large */
+  FA_ERR_HEADDIM = 3, /* d is not 64 or 128 */
+  FA_ERR_PARAM = 4,   /* causal, scale, beta or stable_flag out of range */
+  FA_ERR_ALIGN = 5,   /* a pointer is not aligned as stated above */
+  FA_ERR_HIP = 6      /* a HIP call failed; see fa_last_hip_error() */
+} fa_status;
+
+/* Forward pass: writes o [B,H,N,d] bf16 and lse [B,H,N] fp32.  Same as fa_fwd_ex with
+ * dupcnt = ones = NULL. */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, int causal, float scale, float beta, int stable_flag,
+           void* stream);
+
+/* Forward pass with optional per-row diagnostics (either pointer may be NULL; when either is
+ * non-NULL a variant of the kernel that also counts them runs):
+ *   dupcnt[b,h,i] = number of visible keys j whose score equals the row maximum, i.e.
+ *                   rowsum(S == rowmax(S)) of the ijyty.com article §4.1 / §7.1, computed on the
+ *                   kernel's fp32 dot products;
+ *   ones[b,h,i]   = number of visible keys whose unnormalised probability P^, as rounded to bf16
+ *                   for the P^ V product, equals exactly 1.0.  It depends on the key-block width
+ *                   returned by fa_fwd_kv_block(d), since the shift is chosen per key block from
+ *                   the running (max, count), and key blocks are processed in ascending order. */
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+              int32_t* dupcnt, int32_t* ones,
+              int B, int H, int N, int d, int causal, float scale, float beta, int stable_flag,
+              void* stream);
+
+/* Backward pass: from q, k, v, the forward's o and lse, and the upstream gradient dO, writes
+ * dq, dk, dv [B,H,N,d] bf16.  delta_ws is a caller-owned fp32 workspace of
+ * fa_bwd_workspace_bytes(B,H,N,d) bytes; on return (in stream order) it holds
+ * delta = rowsum(dO o O) per row.  beta and stable_flag are validated like the forward's but do
+ * not change the result: P is rebuilt from lse, which does not depend on the shift. */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dO, void* dq, void* dk, void* dv, float* delta_ws,
+           int B, int H, int N, int d, int causal, float scale, float beta, int stable_flag,
+           void* stream);
+
+/* Backward pass restricted to a subset of its three kernels, in this order when several are set:
+ *   FA_BWD_DELTA (1): delta_ws = rowsum(dO o O);
+ *   FA_BWD_DKDV  (2): dk, dv (reads delta_ws);
+ *   FA_BWD_DQ    (4): dq (reads delta_ws).
+ * fa_bwd == fa_bwd_ex(..., FA_BWD_ALL, stream).  Without FA_BWD_DELTA the caller guarantees that
+ * delta_ws already holds delta for these o and dO (e.g. from an earlier call).  Pointers of
+ * outputs whose stage is not selected are still validated.  stages outside 1..7 -> FA_ERR_PARAM. */
+#define FA_BWD_DELTA 1
+#define FA_BWD_DKDV 2
+#define FA_BWD_DQ 4
+#define FA_BWD_ALL 7
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dO, void* dq, void* dk, void* dv, float* delta_ws,
+              int B, int H, int N, int d, int causal, float scale, float beta, int stable_flag,
+              int stages, void* stream);
+
+/* Bytes of the delta workspace fa_bwd needs: B*H*N*4 (0 for invalid or empty shapes). */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/* Width of the key blocks the forward processes per step for head dimension d (0 if d is not
+ * supported): the granularity at which the running maximum, repeat count and shift change. */
+int fa_fwd_kv_block(int d);
+
+/* Static, human-readable name of a status code. */
+const char* fa_status_str(int status);
+
+/* Raw hipError_t of the last FA_ERR_HIP returned on the calling thread (0 if none). */
+int fa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_STABLE_H */

@@ -1,0 +1,68 @@
+"""Build the HIP library for gfx950: hipcc compiles each translation unit, then links one shared
+library, ``_lib/libfa_stable.so``, next to this file.  Run as ``python
+precision_numerical_stability_amd/build.py`` (``--jobs N`` to limit parallel compiles); it does not
+import the package, which would load the library being rebuilt."""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIBDIR = os.path.join(HERE, "_lib")
+LIBNAME = "libfa_stable.so"
+SOURCES = ("fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip")
+ARCH = "gfx950"
+
+# -packed-fp32-ops keeps the compiler from forming packed fp32 VALU instructions.
+COMMON_FLAGS = [
+    "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found: the ROCm toolchain is required to build the library")
+    return path
+
+
+def _compile(src: str, obj: str, extra) -> None:
+    cmd = [hipcc(), *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed on {src}")
+
+
+def build(jobs: int = 3, extra=()) -> str:
+    os.makedirs(LIBDIR, exist_ok=True)
+    objdir = os.path.join(LIBDIR, "obj")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        futs = [ex.submit(_compile, s, o, list(extra)) for s, o in zip(SOURCES, objs)]
+        for f in futs:
+            f.result()
+    out = os.path.join(LIBDIR, LIBNAME)
+    tmp = out + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("linking libfa_stable.so failed")
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--jobs", type=int, default=3)
+    args = ap.parse_args()
+    print(build(args.jobs))

@@ -1,0 +1,157 @@
+// C ABI of the attention library: argument validation (no HIP call before it passes), template
+// dispatch and launches on the caller's stream.  The library allocates, frees and synchronises
+// nothing and keeps no state apart from a per-thread copy of the last HIP error.
+#include "../../include/fa_stable.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa_launch.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Shared shape/parameter checks.  Returns FA_OK, or the first error found.  *empty is set when
+// the problem has no rows (a successful no-op).
+int check_common(int B, int H, int N, int d, int causal, float scale, float beta, int stable_flag,
+                 bool* empty) {
+  *empty = false;
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (causal != 0 && causal != 1) return FA_ERR_PARAM;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_PARAM;
+  if (!std::isfinite(beta) || !(beta >= 1.f)) return FA_ERR_PARAM;
+  if (stable_flag < 0 || stable_flag > 2) return FA_ERR_PARAM;
+  const int64_t rows = int64_t(B) * int64_t(H) * int64_t(N);
+  if (rows == 0) {
+    *empty = true;
+    return FA_OK;
+  }
+  if (int64_t(B) * int64_t(H) > INT32_MAX / 8) return FA_ERR_SHAPE;
+  if (rows * d >= kMaxElems) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return FA_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* dupcnt,
+              int32_t* ones, int B, int H, int N, int d, int causal, float scale, float beta,
+              int stable_flag, void* stream) {
+  bool empty = false;
+  const int st = check_common(B, H, N, d, causal, scale, beta, stable_flag, &empty);
+  if (st != FA_OK) return st;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return FA_ERR_ALIGN;
+  if (!aligned(lse, 4) || (dupcnt && !aligned(dupcnt, 4)) || (ones && !aligned(ones, 4))) return FA_ERR_ALIGN;
+
+  fa::FwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.dupcnt = dupcnt;
+  a.ones = ones;
+  a.BH = B * H;
+  a.N = N;
+  a.sl2 = scale * 1.4426950408889634f;
+  a.beta = beta;
+  const bool stats = (dupcnt != nullptr) || (ones != nullptr);
+  return hip_status(fa::launch_fwd(a, d, causal != 0, stable_flag, stats, static_cast<hipStream_t>(stream)));
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+           int d, int causal, float scale, float beta, int stable_flag, void* stream) {
+  return fa_fwd_ex(q, k, v, o, lse, nullptr, nullptr, B, H, N, d, causal, scale, beta, stable_flag,
+                   stream);
+}
+
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dO, void* dq, void* dk, void* dv, float* delta_ws, int B, int H, int N,
+              int d, int causal, float scale, float beta, int stable_flag, int stages, void* stream) {
+  bool empty = false;
+  const int st = check_common(B, H, N, d, causal, scale, beta, stable_flag, &empty);
+  if (st != FA_OK) return st;
+  if (stages < 1 || stages > FA_BWD_ALL) return FA_ERR_PARAM;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !delta_ws) return FA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dO, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return FA_ERR_ALIGN;
+  if (!aligned(lse, 4) || !aligned(delta_ws, 4)) return FA_ERR_ALIGN;
+
+  fa::BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.lse = lse;
+  a.dO = static_cast<const uint16_t*>(dO);
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.delta = delta_ws;
+  a.BH = B * H;
+  a.N = N;
+  a.scale = scale;
+  a.sl2 = scale * 1.4426950408889634f;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int rc = FA_OK;
+  if (stages & FA_BWD_DELTA) {
+    rc = hip_status(fa::launch_bwd_delta(a, d, s));
+    if (rc != FA_OK) return rc;
+  }
+  if (stages & FA_BWD_DKDV) {
+    rc = hip_status(fa::launch_bwd_dkdv(a, d, causal != 0, s));
+    if (rc != FA_OK) return rc;
+  }
+  if (stages & FA_BWD_DQ) rc = hip_status(fa::launch_bwd_dq(a, d, causal != 0, s));
+  return rc;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dO, void* dq, void* dk, void* dv, float* delta_ws, int B, int H, int N, int d,
+           int causal, float scale, float beta, int stable_flag, void* stream) {
+  return fa_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, delta_ws, B, H, N, d, causal, scale, beta,
+                   stable_flag, FA_BWD_ALL, stream);
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if (B < 0 || H < 0 || N < 0 || (d != 64 && d != 128)) return 0;
+  return size_t(B) * size_t(H) * size_t(N) * sizeof(float);
+}
+
+int fa_fwd_kv_block(int d) { return fa::fwd_kv_block(d); }
+
+const char* fa_status_str(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: B, H or N negative, or the problem is too large";
+    case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: d must be 64 or 128";
+    case FA_ERR_PARAM: return "FA_ERR_PARAM: causal, scale, beta or stable_flag out of range";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensor pointers must be 16-byte aligned, vectors 4-byte";
+    case FA_ERR_HIP: return "FA_ERR_HIP: a HIP call failed (see fa_last_hip_error)";
+    default: return "unknown fa_status";
+  }
+}
+
+int fa_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,393 @@
+// Backward kernels: delta = rowsum(dO o O), then dK/dV and dQ by recomputing P from the saved
+// logsumexp.
+//
+// Follows the backward by recomputation of "FlashAttention 训练时为什么会梯度爆炸？一次拆透反向
+// 传播的坑" (cnnetsun.cn/a/2497354) §2 -- keep no probability matrix, rebuild it from Q, K and the
+// saved row statistics -- and the preprocessing term delta of the BF16 Flash Attention article
+// (ijyty.com/news/896914) §3.1.  With S = scale Q K^T and P = exp(S - LSE):
+//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - delta),  dQ = scale dS K,  dK = scale dS^T Q.
+// P does not depend on the forward's shift: LSE = m + ln l is the same for every shift.
+//
+// dK/dV and dQ run as two kernels with no atomics: each output tile is owned by exactly one
+// workgroup, so results are deterministic.  All three run on the caller's stream in order.
+#include "fa_common.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+
+constexpr int kThreads = 256;
+
+// ---------------------------------------------------------------------------------------------
+// delta[row] = sum_c dO[row, c] * O[row, c], bf16 inputs, fp32 arithmetic.  HBM-bound: one
+// 16-byte load of O and of dO per thread, D / 8 threads per row.
+template <int D>
+__global__ __launch_bounds__(kThreads) void delta_kernel(BwdArgs a) {
+  constexpr int TPR = D / 8;
+  constexpr int RPB = kThreads / TPR;
+  const int tid = threadIdx.x;
+  const int64_t total = (int64_t)a.BH * a.N;
+  const int64_t row = (int64_t)blockIdx.x * RPB + tid / TPR;
+  const int c = tid % TPR;
+  float acc = 0.f;
+  if (row < total) {
+    const i32x4 ov = *reinterpret_cast<const i32x4*>(a.o + row * D + 8 * c);
+    const i32x4 gv = *reinterpret_cast<const i32x4*>(a.dO + row * D + 8 * c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t ow = (uint32_t)ov[i];
+      const uint32_t gw = (uint32_t)gv[i];
+      const float o_lo = __builtin_bit_cast(float, ow << 16);
+      const float o_hi = __builtin_bit_cast(float, ow & 0xFFFF0000u);
+      const float g_lo = __builtin_bit_cast(float, gw << 16);
+      const float g_hi = __builtin_bit_cast(float, gw & 0xFFFF0000u);
+      acc = fmaf(o_lo, g_lo, acc);
+      acc = fmaf(o_hi, g_hi, acc);
+    }
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (c == 0 && row < total) a.delta[row] = acc;
+}
+
+// ---------------------------------------------------------------------------------------------
+// dQ: one workgroup per (128-query tile, head), 4 waves of 32 queries; loops over 64-key blocks.
+// Lane layout as in the forward: S^T = K Q^T and dP^T = V dO^T put one query per lane, so LSE
+// and delta are lane-local; dQ^T = K^T dS^T takes dS^T from the accumulator registers.
+constexpr int kDqBc = 64;
+constexpr int kDqBr = 128;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
+  constexpr int BC = kDqBc, BR = kDqBr, KS = D / 16, DT = D / 32, KB = BC / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BC * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BC * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  int bh, rank;
+  map_block(blockIdx.x, a.BH, a.n_tiles, bh, rank);
+  const int qt = CAUSAL ? a.n_tiles - 1 - rank : rank;
+  const int N = a.N;
+  const int q0 = qt * BR;
+  const int64_t hoff = (int64_t)bh * N * D;
+  const uint16_t* Kg = a.k + hoff;
+  const uint16_t* Vg = a.v + hoff;
+  const int qw0 = q0 + wave * 32;
+  const int qrow = qw0 + l32;
+  const int qsrc = min(qrow, N - 1);
+
+  bf16x8 qf[KS], gf[KS];
+  {
+    const uint16_t* qs = a.q + hoff + (int64_t)qsrc * D + 8 * hh;
+    const uint16_t* gs = a.dO + hoff + (int64_t)qsrc * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = as_bf16x8(*reinterpret_cast<const i32x4*>(qs + 16 * ks));
+      gf[ks] = as_bf16x8(*reinterpret_cast<const i32x4*>(gs + 16 * ks));
+    }
+  }
+  const float lse2 = a.lse[(int64_t)bh * N + qsrc] * kLog2e;
+  const float dlt = a.delta[(int64_t)bh * N + qsrc];
+
+  int n_kv = (N + BC - 1) / BC;
+  if (CAUSAL) n_kv = min(n_kv, (q0 + BR - 1) / BC + 1);
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
+
+  TileStage<BC, D, kThreads> stK, stV;
+  stK.load(Kg, 0, N, tid);
+  stV.load(Vg, 0, N, tid);
+  stK.store(sK[0], tid);
+  stV.store(sV[0], tid);
+  __syncthreads();
+
+  for (int j = 0; j < n_kv; ++j) {
+    const int buf = j & 1;
+    const int kv0 = j * BC;
+    const bool has_next = (j + 1 < n_kv);
+    if (has_next) {
+      stK.load(Kg, kv0 + BC, N, tid);
+      stV.load(Vg, kv0 + BC, N, tid);
+    }
+    const bool active = !CAUSAL || (kv0 <= qw0 + 31);
+    if (active) {
+      const uint16_t* tK = sK[buf];
+      const uint16_t* tV = sV[buf];
+      const bool need_mask = CAUSAL ? (kv0 + BC - 1 > qw0) : (kv0 + BC > N);
+      uint32_t pds[KB][8];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 kf = lds_read_row8<D>(tK, 32 * kb + l32, 16 * ks + 8 * hh);
+          const bf16x8 vf = lds_read_row8<D>(tV, 32 * kb + l32, 16 * ks + 8 * hh);
+          s = mfma32x32x16(kf, qf[ks], s);
+          dp = mfma32x32x16(vf, gf[ks], dp);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          float ds2[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int rr = r + u;
+            float p = fast_exp2(fmaf(s[rr], a.sl2, -lse2));
+            if (need_mask) {
+              const int key = kv0 + 32 * kb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+              const bool hide = (key >= N) || (CAUSAL && key > qrow);
+              p = hide ? 0.f : p;
+            }
+            ds2[u] = p * (dp[rr] - dlt);
+          }
+          pds[kb][r >> 1] = pack_bf16x2(ds2[0], ds2[1]);
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < BC / 16; ++kk) {
+        const int kb = kk >> 1;
+        const int o4 = (kk & 1) * 4;
+        const bf16x8 db = make_bf16x8(pds[kb][o4], pds[kb][o4 + 1], pds[kb][o4 + 2], pds[kb][o4 + 3]);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const bf16x8 kt = lds_read_col8_tr<D>(tK, 16 * kk, 32 * dt, lane);
+          acc[dt] = mfma32x32x16(kt, db, acc[dt]);
+        }
+      }
+    }
+    if (has_next) {
+      stK.store(sK[buf ^ 1], tid);
+      stV.store(sV[buf ^ 1], tid);
+    }
+    __syncthreads();
+  }
+
+  if (qrow < N) {
+    uint16_t* dst = a.dq + hoff + (int64_t)qrow * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int d0 = 32 * dt + 8 * rr + 4 * hh;
+        i32x2 w;
+        w[0] = (int)pack_bf16x2(acc[dt][4 * rr] * a.scale, acc[dt][4 * rr + 1] * a.scale);
+        w[1] = (int)pack_bf16x2(acc[dt][4 * rr + 2] * a.scale, acc[dt][4 * rr + 3] * a.scale);
+        *reinterpret_cast<i32x2*>(dst + d0) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// dK/dV: one workgroup per (128-key tile, head), 4 waves of 32 keys; loops over 64-query blocks.
+// S = Q K^T and dP = dO V^T put one key per lane (K and V stay in registers as B operands);
+// dV^T = dO^T P and dK^T = Q^T dS take P and dS from the accumulator registers, with dO^T and
+// Q^T read transposed from LDS.  The per-query LSE and delta come from LDS as 4-float vectors.
+constexpr int kDkvBq = 64;
+constexpr int kDkvBk = 128;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
+  constexpr int BQ = kDkvBq, BK = kDkvBk, KS = D / 16, DT = D / 32, QB = BQ / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sG[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) float sL[2][BQ];
+  __shared__ __attribute__((aligned(16))) float sD[2][BQ];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  int bh, rank;
+  map_block(blockIdx.x, a.BH, a.n_tiles, bh, rank);
+  const int kt = rank;  // causal: the first key tiles see the most queries, so they start first
+  const int N = a.N;
+  const int k0 = kt * BK;
+  const int64_t hoff = (int64_t)bh * N * D;
+  const int64_t roff = (int64_t)bh * N;
+  const uint16_t* Qg = a.q + hoff;
+  const uint16_t* Gg = a.dO + hoff;
+  const int kw0 = k0 + wave * 32;
+  const int key = kw0 + l32;
+  const int ksrc = min(key, N - 1);
+
+  bf16x8 kf[KS], vf[KS];
+  {
+    const uint16_t* ks_ = a.k + hoff + (int64_t)ksrc * D + 8 * hh;
+    const uint16_t* vs_ = a.v + hoff + (int64_t)ksrc * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = as_bf16x8(*reinterpret_cast<const i32x4*>(ks_ + 16 * ks));
+      vf[ks] = as_bf16x8(*reinterpret_cast<const i32x4*>(vs_ + 16 * ks));
+    }
+  }
+
+  const int n_q = (N + BQ - 1) / BQ;
+  const int i_first = CAUSAL ? (k0 / BQ) : 0;
+
+  f32x16 dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    dk[dt] = zero16();
+    dv[dt] = zero16();
+  }
+
+  TileStage<BQ, D, kThreads> stQ, stG;
+  float vl = 0.f, vd = 0.f;
+  auto stage_load = [&](int i) {
+    const int qq0 = i * BQ;
+    stQ.load(Qg, qq0, N, tid);
+    stG.load(Gg, qq0, N, tid);
+    if (tid < BQ) {
+      const int64_t src = roff + min(qq0 + tid, N - 1);
+      vl = a.lse[src] * kLog2e;
+      vd = a.delta[src];
+    }
+  };
+  auto stage_store = [&](int b) {
+    stQ.store(sQ[b], tid);
+    stG.store(sG[b], tid);
+    if (tid < BQ) {
+      sL[b][tid] = vl;
+      sD[b][tid] = vd;
+    }
+  };
+
+  if (i_first < n_q) {
+    stage_load(i_first);
+    stage_store(0);
+  }
+  __syncthreads();
+
+  for (int i = i_first; i < n_q; ++i) {
+    const int buf = (i - i_first) & 1;
+    const int q0 = i * BQ;
+    const bool has_next = (i + 1 < n_q);
+    if (has_next) stage_load(i + 1);
+    // A wave whose keys all follow every query of this block sees nothing in it.
+    const bool active = !CAUSAL || (q0 + BQ - 1 >= kw0);
+    if (active) {
+      const uint16_t* tQ = sQ[buf];
+      const uint16_t* tG = sG[buf];
+      const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (q0 + BQ > N);
+      uint32_t pp[QB][8], pd[QB][8];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 qa = lds_read_row8<D>(tQ, 32 * qb + l32, 16 * ks + 8 * hh);
+          const bf16x8 ga = lds_read_row8<D>(tG, 32 * qb + l32, 16 * ks + 8 * hh);
+          s = mfma32x32x16(qa, kf[ks], s);
+          dp = mfma32x32x16(ga, vf[ks], dp);
+        }
+        // Rows of s/dp here are queries 32 qb + 8 (r/4) + 4 hh + (r%4); column = this lane's key.
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int qi = 32 * qb + 8 * rq + 4 * hh;
+          const float4 l4 = *reinterpret_cast<const float4*>(&sL[buf][qi]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&sD[buf][qi]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+          float pv[4], dsv[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int r = 4 * rq + u;
+            float p = fast_exp2(fmaf(s[r], a.sl2, -lv[u]));
+            if (need_mask) {
+              const int qidx = q0 + qi + u;
+              const bool hide = (qidx >= N) || (CAUSAL && key > qidx);
+              p = hide ? 0.f : p;
+            }
+            pv[u] = p;
+            dsv[u] = p * (dp[r] - dv4[u]);
+          }
+          pp[qb][2 * rq] = pack_bf16x2(pv[0], pv[1]);
+          pp[qb][2 * rq + 1] = pack_bf16x2(pv[2], pv[3]);
+          pd[qb][2 * rq] = pack_bf16x2(dsv[0], dsv[1]);
+          pd[qb][2 * rq + 1] = pack_bf16x2(dsv[2], dsv[3]);
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < BQ / 16; ++kk) {
+        const int qb = kk >> 1;
+        const int o4 = (kk & 1) * 4;
+        const bf16x8 pb = make_bf16x8(pp[qb][o4], pp[qb][o4 + 1], pp[qb][o4 + 2], pp[qb][o4 + 3]);
+        const bf16x8 sb = make_bf16x8(pd[qb][o4], pd[qb][o4 + 1], pd[qb][o4 + 2], pd[qb][o4 + 3]);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const bf16x8 gt = lds_read_col8_tr<D>(tG, 16 * kk, 32 * dt, lane);
+          const bf16x8 qt = lds_read_col8_tr<D>(tQ, 16 * kk, 32 * dt, lane);
+          dv[dt] = mfma32x32x16(gt, pb, dv[dt]);
+          dk[dt] = mfma32x32x16(qt, sb, dk[dt]);
+        }
+      }
+    }
+    if (has_next) stage_store(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (key < N) {
+    uint16_t* dkr = a.dk + hoff + (int64_t)key * D;
+    uint16_t* dvr = a.dv + hoff + (int64_t)key * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int d0 = 32 * dt + 8 * rr + 4 * hh;
+        i32x2 wk, wv;
+        wk[0] = (int)pack_bf16x2(dk[dt][4 * rr] * a.scale, dk[dt][4 * rr + 1] * a.scale);
+        wk[1] = (int)pack_bf16x2(dk[dt][4 * rr + 2] * a.scale, dk[dt][4 * rr + 3] * a.scale);
+        wv[0] = (int)pack_bf16x2(dv[dt][4 * rr], dv[dt][4 * rr + 1]);
+        wv[1] = (int)pack_bf16x2(dv[dt][4 * rr + 2], dv[dt][4 * rr + 3]);
+        *reinterpret_cast<i32x2*>(dkr + d0) = wk;
+        *reinterpret_cast<i32x2*>(dvr + d0) = wv;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+hipError_t launch_bwd_delta(BwdArgs a, int d, hipStream_t s) {
+  const int64_t total = (int64_t)a.BH * a.N;
+  const int rpb = kThreads / (d / 8);
+  const int64_t grid = (total + rpb - 1) / rpb;
+  if (d == 64)
+    hipLaunchKernelGGL(delta_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(delta_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(BwdArgs a, int d, bool causal, hipStream_t s) {
+  a.n_tiles = (a.N + kDqBr - 1) / kDqBr;
+  const dim3 grid(a.n_tiles * a.BH);
+  if (d == 64) {
+    if (causal) hipLaunchKernelGGL((dq_kernel<64, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((dq_kernel<64, false>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    if (causal) hipLaunchKernelGGL((dq_kernel<128, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((dq_kernel<128, false>), grid, dim3(kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv(BwdArgs a, int d, bool causal, hipStream_t s) {
+  a.n_tiles = (a.N + kDkvBk - 1) / kDkvBk;
+  const dim3 grid(a.n_tiles * a.BH);
+  if (d == 64) {
+    if (causal) hipLaunchKernelGGL((dkdv_kernel<64, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((dkdv_kernel<64, false>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    if (causal) hipLaunchKernelGGL((dkdv_kernel<128, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((dkdv_kernel<128, false>), grid, dim3(kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -1,0 +1,178 @@
+// Device primitives for the gfx950 attention kernels: MFMA wrappers, bf16 packing, swizzled LDS
+// tiles, the LDS transpose read, and half-wave reductions.
+//
+// Register layouts (v_mfma_f32_32x32x16_bf16, one wave of 64 lanes, h = lane / 32):
+//   A operand (32 x 16):  lane l holds A[l % 32][8h .. 8h + 7]
+//   B operand (16 x 32):  lane l holds B[8h .. 8h + 7][l % 32]
+//   C/D (32 x 32 fp32):   lane l, register r holds C[8 (r / 4) + 4 h + (r % 4)][l % 32]
+// Only the pairing of A's and B's k-slots matters for a product, so an operand may carry its k
+// values in any order as long as the other operand uses the same order.  The kernels use this to
+// feed the C layout of one product straight into the B operand of the next: within each 16-wide
+// k slab, slot t of half h holds index 4h + t (t < 4) or 8 + 4h + (t - 4) (t >= 4), which is what
+// C registers 8s .. 8s + 7 of slab s hold.
+//
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane s supplies the address of 4 consecutive
+// 16-bit elements (row s / 4, columns 4 (s % 4) .. + 3 of a 4 x 16 block) and lane o receives
+// column o of that block, rows 0..3.  This yields 4 consecutive k values of one output column,
+// i.e. the transposed operand, from a row-major tile.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr uint16_t kBf16One = 0x3F80;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Two fp32 -> packed bf16 pair (round to nearest even), low half = a.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 r = __builtin_convertvector((f32x2){a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(i32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ bf16x8 make_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  i32x4 v = {(int)a, (int)b, (int)c, (int)d};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Reductions over the two 32-lane halves of a wave: lane l and lane l ^ 32 both receive the
+// combined value.  v_permlane32_swap exchanges the first operand of the upper half with the
+// second operand of the lower half, so applied to (x, x) each lane ends up holding both its own
+// and its partner's x, in an order that differs by half; max and + are symmetric in it.
+__device__ __forceinline__ float halves_max(float x) {
+  int xi = __builtin_bit_cast(int, x);
+  auto s = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return fmaxf(__builtin_bit_cast(float, (int)s[0]), __builtin_bit_cast(float, (int)s[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  int xi = __builtin_bit_cast(int, x);
+  auto s = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return __builtin_bit_cast(float, (int)s[0]) + __builtin_bit_cast(float, (int)s[1]);
+}
+__device__ __forceinline__ int halves_sum_i(int x) {
+  auto s = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return (int)s[0] + (int)s[1];
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------------------------
+// Swizzled row-major [rows][D] bf16 tiles in LDS.  The 16-byte chunk c of row r is stored at
+// chunk c ^ f(r).  f is chosen so that (a) 16 consecutive rows read at the same logical chunk
+// (the 16-byte operand reads) land in distinct chunk positions, and (b) the 4 rows of one
+// transpose-read block, read at an aligned chunk pair, occupy distinct chunk pairs.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) {
+    return ((row & 3) << 1) | (((row >> 2) & 1) << 3) | ((row >> 3) & 1);
+  } else {
+    return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+  }
+}
+
+// Element offset of (row, col) in a swizzled [rows][D] tile.
+template <int D>
+__device__ __forceinline__ int lds_off(int row, int col) {
+  return row * D + ((((col >> 3) ^ swz<D>(row))) << 3) + (col & 7);
+}
+
+// 16-byte operand read: row `row`, columns col .. col + 7 (col a multiple of 8).
+template <int D>
+__device__ __forceinline__ bf16x8 lds_read_row8(const uint16_t* tile, int row, int col) {
+  return as_bf16x8(*reinterpret_cast<const i32x4*>(tile + lds_off<D>(row, col)));
+}
+
+// Transposed operand read: this lane receives column (col0 + (lane % 32)) at the eight rows
+// row0 + 4h + {0,1,2,3} and row0 + 8 + 4h + {0,1,2,3} (h = lane / 32), in that slot order.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_read_col8_tr(const uint16_t* tile, int row0, int col0, int lane) {
+  const int s = lane & 15;
+  const int g = lane >> 4;
+  const int h = lane >> 5;
+  const int col = col0 + ((g & 1) << 4) + ((s & 3) << 2);
+  const int r1 = row0 + (h << 2) + (s >> 2);
+  const uint16_t* p1 = tile + lds_off<D>(r1, col);
+  const uint16_t* p2 = tile + lds_off<D>(r1 + 8, col);
+  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p2));
+  i32x2 a = __builtin_bit_cast(i32x2, lo);
+  i32x2 b = __builtin_bit_cast(i32x2, hi);
+  return make_bf16x8((uint32_t)a[0], (uint32_t)a[1], (uint32_t)b[0], (uint32_t)b[1]);
+}
+
+// Cooperative copy of a ROWS x D bf16 tile (rows row0 .. row0 + ROWS - 1 of a [n_rows][D] head)
+// from global memory into registers, then into a swizzled LDS tile.  Rows at or past n_rows are
+// read from row n_rows - 1 instead (valid memory; the kernels mask those keys/queries).
+template <int ROWS, int D, int NT>
+struct TileStage {
+  static constexpr int kChunksPerRow = D / 8;
+  static constexpr int kChunks = ROWS * kChunksPerRow;
+  static constexpr int kPer = kChunks / NT;
+  static_assert(kChunks % NT == 0, "tile must split evenly over the threads");
+  i32x4 buf[kPer];
+
+  __device__ __forceinline__ void load(const uint16_t* head, int row0, int n_rows, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int ch = tid + i * NT;
+      const int r = ch / kChunksPerRow;
+      const int c = ch % kChunksPerRow;
+      const int gr = min(row0 + r, n_rows - 1);
+      buf[i] = *reinterpret_cast<const i32x4*>(head + (int64_t)gr * D + c * 8);
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* tile, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int ch = tid + i * NT;
+      const int r = ch / kChunksPerRow;
+      const int c = ch % kChunksPerRow;
+      *reinterpret_cast<i32x4*>(tile + r * D + ((c ^ swz<D>(r)) << 3)) = buf[i];
+    }
+  }
+};
+
+// Workgroup -> (head, tile rank).  The hardware hands consecutive workgroup ids to the 8 XCDs in
+// turn, so when the head count divides by 8, id x runs on XCD x % 8 and that XCD is given the
+// heads congruent to it: the concurrently running tiles of a head then share one XCD's L2.
+// Ranks are walked in order within an XCD, so the longest (rank 0) tiles start first.
+__device__ __forceinline__ void map_block(int x, int n_heads, int n_tiles, int& head, int& rank) {
+  if ((n_heads & 7) == 0) {
+    const int xcd = x & 7;
+    const int slot = x >> 3;
+    const int per = n_heads >> 3;
+    rank = slot / per;
+    head = xcd + 8 * (slot % per);
+  } else {
+    rank = x / n_heads;
+    head = x % n_heads;
+  }
+  (void)n_tiles;
+}
+
+}  // namespace fa

@@ -1,0 +1,50 @@
+// Internal interface between the C ABI (fa_api.cpp) and the kernel translation units.
+// Arguments here are already validated; these functions only launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int32_t* dupcnt;  // may be null
+  int32_t* ones;    // may be null
+  int BH;           // B * H
+  int N;
+  int n_tiles;      // query tiles per head (set by launch_fwd)
+  float sl2;        // scale * log2(e)
+  float beta;
+};
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const float* lse;
+  const uint16_t* dO;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* delta;
+  int BH;
+  int N;
+  int n_tiles;  // set by each launcher
+  float scale;
+  float sl2;    // scale * log2(e)
+};
+
+hipError_t launch_fwd(FwdArgs a, int d, bool causal, int mode, bool stats, hipStream_t s);
+hipError_t launch_bwd_delta(BwdArgs a, int d, hipStream_t s);
+hipError_t launch_bwd_dkdv(BwdArgs a, int d, bool causal, hipStream_t s);
+hipError_t launch_bwd_dq(BwdArgs a, int d, bool causal, hipStream_t s);
+int fwd_kv_block(int d);
+int fwd_q_block(int d);
+
+}  // namespace fa
