@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--mode", type=int, default=1, help="stable_flag: 0, 1 or 2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-iters", type=int, default=20)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one device-to-device copy of this many MiB (to scale HBM "
+                         "traffic counters against a transfer of known size)")
     return ap.parse_args()
 
 
@@ -133,6 +136,14 @@ def main():
     ms_dq = time_events(run_stage(fa.FA_BWD_DQ), it, stream)
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all() and torch.isfinite(dq.float()).all()
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     ff = fwd_flops(B, H, N, d, causal)
     total = 3.5 * ff

@@ -22,7 +22,8 @@
  *     lse holds the natural-log logsumexp of the scaled scores: LSE = m + ln(l).
  *   - dupcnt, ones: device pointers to contiguous [B, H, N] int32, 4-byte aligned.
  *   - B, H, N >= 0 (an empty problem, B*H*N == 0, is a successful no-op); d is 64 or 128.
- *     N need not be a multiple of any tile size.  B*H*N*d < 2^40.
+ *     N need not be a multiple of any tile size.  B*H*N*d < 2^40 and N*d*2 < 2^31 (one head
+ *     spans less than 2 GiB).
  *   - causal: 0 or 1; causal masking is top-left aligned (key j is visible to query i iff j <= i).
  *   - scale: the score scale (typically 1/sqrt(d)), finite and > 0.
  *   - beta: the shift factor for positive repeated maxima, finite and >= 1 (1.25 recommended by

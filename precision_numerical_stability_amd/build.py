@@ -57,8 +57,20 @@ def build(jobs: int = 3, extra=()) -> str:
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("linking libfa_stable.so failed")
+    _check_no_undefined_stubs(tmp)
     os.replace(tmp, out)
     return out
+
+
+def _check_no_undefined_stubs(lib: str) -> None:
+    """Fail the build if the library references a kernel launch stub it does not define."""
+    nm = shutil.which("nm")
+    if nm is None:
+        return
+    res = subprocess.run([nm, "-D", "--undefined-only", lib], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in res.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        raise RuntimeError(f"{len(missing)} kernel launch stubs are undefined in {lib}, e.g. {missing[0]}")
 
 
 if __name__ == "__main__":

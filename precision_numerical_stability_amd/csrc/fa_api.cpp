@@ -36,6 +36,8 @@ int check_common(int B, int H, int N, int d, int causal, float scale, float beta
   }
   if (int64_t(B) * int64_t(H) > INT32_MAX / 8) return FA_ERR_SHAPE;
   if (rows * d >= kMaxElems) return FA_ERR_SHAPE;
+  // One head's rows are addressed through 32-bit buffer ranges.
+  if (int64_t(N) * d * 2 > int64_t(INT32_MAX)) return FA_ERR_SHAPE;
   return FA_OK;
 }
 

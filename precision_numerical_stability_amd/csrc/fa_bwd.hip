@@ -52,7 +52,9 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------------------------
 // dQ: one workgroup per (128-query tile, head), 4 waves of 32 queries; loops over 64-key blocks.
 // Lane layout as in the forward: S^T = K Q^T and dP^T = V dO^T put one query per lane, so LSE
-// and delta are lane-local; dQ^T = K^T dS^T takes dS^T from the accumulator registers.
+// and delta are lane-local; dQ^T = K^T dS^T takes dS^T from the accumulator registers.  Each
+// 32-key half of a block is finished (S, dP, dS, its dQ products) before the next, which keeps
+// only one half's scores in registers.
 constexpr int kDqBc = 64;
 constexpr int kDqBr = 128;
 
@@ -100,27 +102,25 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
 
-  TileStage<BC, D, kThreads> stK, stV;
-  stK.load(Kg, 0, N, tid);
-  stV.load(Vg, 0, N, tid);
-  stK.store(sK[0], tid);
-  stV.store(sV[0], tid);
+  DirectStage<BC, D, kThreads> st;
+  st.init(tid);
+  st.issue(Kg, 0, N, sK[0]);
+  st.issue(Vg, 0, N, sV[0]);
+  wait_vm0();
   __syncthreads();
 
   for (int j = 0; j < n_kv; ++j) {
     const int buf = j & 1;
     const int kv0 = j * BC;
-    const bool has_next = (j + 1 < n_kv);
-    if (has_next) {
-      stK.load(Kg, kv0 + BC, N, tid);
-      stV.load(Vg, kv0 + BC, N, tid);
+    if (j + 1 < n_kv) {
+      st.issue(Kg, kv0 + BC, N, sK[buf ^ 1]);
+      st.issue(Vg, kv0 + BC, N, sV[buf ^ 1]);
     }
     const bool active = !CAUSAL || (kv0 <= qw0 + 31);
     if (active) {
       const uint16_t* tK = sK[buf];
       const uint16_t* tV = sV[buf];
       const bool need_mask = CAUSAL ? (kv0 + BC - 1 > qw0) : (kv0 + BC > N);
-      uint32_t pds[KB][8];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         f32x16 s = zero16(), dp = zero16();
@@ -131,6 +131,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
           s = mfma32x32x16(kf, qf[ks], s);
           dp = mfma32x32x16(vf, gf[ks], dp);
         }
+        uint32_t pds[8];
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
           float ds2[2];
@@ -145,25 +146,21 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
             }
             ds2[u] = p * (dp[rr] - dlt);
           }
-          pds[kb][r >> 1] = pack_bf16x2(ds2[0], ds2[1]);
+          pds[r >> 1] = pack_bf16x2(ds2[0], ds2[1]);
         }
-      }
 #pragma unroll
-      for (int kk = 0; kk < BC / 16; ++kk) {
-        const int kb = kk >> 1;
-        const int o4 = (kk & 1) * 4;
-        const bf16x8 db = make_bf16x8(pds[kb][o4], pds[kb][o4 + 1], pds[kb][o4 + 2], pds[kb][o4 + 3]);
+        for (int half = 0; half < 2; ++half) {
+          const int kk = 2 * kb + half;
+          const bf16x8 db = make_bf16x8(pds[4 * half], pds[4 * half + 1], pds[4 * half + 2], pds[4 * half + 3]);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const bf16x8 kt = lds_read_col8_tr<D>(tK, 16 * kk, 32 * dt, lane);
-          acc[dt] = mfma32x32x16(kt, db, acc[dt]);
+          for (int dt = 0; dt < DT; ++dt) {
+            const bf16x8 kt = lds_read_col8_tr<D>(tK, 16 * kk, 32 * dt, lane);
+            acc[dt] = mfma32x32x16(kt, db, acc[dt]);
+          }
         }
       }
     }
-    if (has_next) {
-      stK.store(sK[buf ^ 1], tid);
-      stV.store(sV[buf ^ 1], tid);
-    }
+    wait_vm0();
     __syncthreads();
   }
 
@@ -187,6 +184,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
 // S = Q K^T and dP = dO V^T put one key per lane (K and V stay in registers as B operands);
 // dV^T = dO^T P and dK^T = Q^T dS take P and dS from the accumulator registers, with dO^T and
 // Q^T read transposed from LDS.  The per-query LSE and delta come from LDS as 4-float vectors.
+// Each 32-query half of a block is finished before the next.
 constexpr int kDkvBq = 64;
 constexpr int kDkvBk = 128;
 
@@ -238,21 +236,17 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
     dv[dt] = zero16();
   }
 
-  TileStage<BQ, D, kThreads> stQ, stG;
+  DirectStage<BQ, D, kThreads> st;
+  st.init(tid);
   float vl = 0.f, vd = 0.f;
-  auto stage_load = [&](int i) {
-    const int qq0 = i * BQ;
-    stQ.load(Qg, qq0, N, tid);
-    stG.load(Gg, qq0, N, tid);
+  auto load_rows = [&](int i) {
     if (tid < BQ) {
-      const int64_t src = roff + min(qq0 + tid, N - 1);
+      const int64_t src = roff + min(i * BQ + tid, N - 1);
       vl = a.lse[src] * kLog2e;
       vd = a.delta[src];
     }
   };
-  auto stage_store = [&](int b) {
-    stQ.store(sQ[b], tid);
-    stG.store(sG[b], tid);
+  auto store_rows = [&](int b) {
     if (tid < BQ) {
       sL[b][tid] = vl;
       sD[b][tid] = vd;
@@ -260,23 +254,29 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   };
 
   if (i_first < n_q) {
-    stage_load(i_first);
-    stage_store(0);
+    st.issue(Qg, i_first * BQ, N, sQ[0]);
+    st.issue(Gg, i_first * BQ, N, sG[0]);
+    load_rows(i_first);
+    store_rows(0);
   }
+  wait_vm0();
   __syncthreads();
 
   for (int i = i_first; i < n_q; ++i) {
     const int buf = (i - i_first) & 1;
     const int q0 = i * BQ;
     const bool has_next = (i + 1 < n_q);
-    if (has_next) stage_load(i + 1);
+    if (has_next) {
+      st.issue(Qg, q0 + BQ, N, sQ[buf ^ 1]);
+      st.issue(Gg, q0 + BQ, N, sG[buf ^ 1]);
+      load_rows(i + 1);
+    }
     // A wave whose keys all follow every query of this block sees nothing in it.
     const bool active = !CAUSAL || (q0 + BQ - 1 >= kw0);
     if (active) {
       const uint16_t* tQ = sQ[buf];
       const uint16_t* tG = sG[buf];
       const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (q0 + BQ > N);
-      uint32_t pp[QB][8], pd[QB][8];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         f32x16 s = zero16(), dp = zero16();
@@ -288,6 +288,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
           dp = mfma32x32x16(ga, vf[ks], dp);
         }
         // Rows of s/dp here are queries 32 qb + 8 (r/4) + 4 hh + (r%4); column = this lane's key.
+        uint32_t pp[8], pd[8];
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
           const int qi = 32 * qb + 8 * rq + 4 * hh;
@@ -308,28 +309,29 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
             pv[u] = p;
             dsv[u] = p * (dp[r] - dv4[u]);
           }
-          pp[qb][2 * rq] = pack_bf16x2(pv[0], pv[1]);
-          pp[qb][2 * rq + 1] = pack_bf16x2(pv[2], pv[3]);
-          pd[qb][2 * rq] = pack_bf16x2(dsv[0], dsv[1]);
-          pd[qb][2 * rq + 1] = pack_bf16x2(dsv[2], dsv[3]);
+          pp[2 * rq] = pack_bf16x2(pv[0], pv[1]);
+          pp[2 * rq + 1] = pack_bf16x2(pv[2], pv[3]);
+          pd[2 * rq] = pack_bf16x2(dsv[0], dsv[1]);
+          pd[2 * rq + 1] = pack_bf16x2(dsv[2], dsv[3]);
         }
-      }
 #pragma unroll
-      for (int kk = 0; kk < BQ / 16; ++kk) {
-        const int qb = kk >> 1;
-        const int o4 = (kk & 1) * 4;
-        const bf16x8 pb = make_bf16x8(pp[qb][o4], pp[qb][o4 + 1], pp[qb][o4 + 2], pp[qb][o4 + 3]);
-        const bf16x8 sb = make_bf16x8(pd[qb][o4], pd[qb][o4 + 1], pd[qb][o4 + 2], pd[qb][o4 + 3]);
+        for (int half = 0; half < 2; ++half) {
+          const int kk = 2 * qb + half;
+          const int o4 = 4 * half;
+          const bf16x8 pb = make_bf16x8(pp[o4], pp[o4 + 1], pp[o4 + 2], pp[o4 + 3]);
+          const bf16x8 sb = make_bf16x8(pd[o4], pd[o4 + 1], pd[o4 + 2], pd[o4 + 3]);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const bf16x8 gt = lds_read_col8_tr<D>(tG, 16 * kk, 32 * dt, lane);
-          const bf16x8 qt = lds_read_col8_tr<D>(tQ, 16 * kk, 32 * dt, lane);
-          dv[dt] = mfma32x32x16(gt, pb, dv[dt]);
-          dk[dt] = mfma32x32x16(qt, sb, dk[dt]);
+          for (int dt = 0; dt < DT; ++dt) {
+            const bf16x8 gt = lds_read_col8_tr<D>(tG, 16 * kk, 32 * dt, lane);
+            const bf16x8 qt = lds_read_col8_tr<D>(tQ, 16 * kk, 32 * dt, lane);
+            dv[dt] = mfma32x32x16(gt, pb, dv[dt]);
+            dk[dt] = mfma32x32x16(qt, sb, dk[dt]);
+          }
         }
       }
     }
-    if (has_next) stage_store(buf ^ 1);
+    if (has_next) store_rows(buf ^ 1);
+    wait_vm0();
     __syncthreads();
   }
 

@@ -83,16 +83,15 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // ---------------------------------------------------------------------------------------------
 // Swizzled row-major [rows][D] bf16 tiles in LDS.  The 16-byte chunk c of row r is stored at
-// chunk c ^ f(r).  f is chosen so that (a) 16 consecutive rows read at the same logical chunk
-// (the 16-byte operand reads) land in distinct chunk positions, and (b) the 4 rows of one
-// transpose-read block, read at an aligned chunk pair, occupy distinct chunk pairs.
+// chunk c ^ f(r), f(r) = 2 (r mod 4) + (r / 4) mod 2.  With 32 four-byte banks (128 bytes per
+// cycle), a 16-byte operand read serves 8 lanes per cycle -- 8 consecutive rows at the same
+// logical chunk -- and f(r) mod 8 is distinct over any 8 consecutive rows; a transpose read
+// serves one 16-lane group per cycle -- 4 consecutive rows (aligned to 4) at an aligned chunk
+// pair -- and f(r) / 2 is distinct over those 4 rows.  Both patterns are therefore free of bank
+// conflicts, for d = 64 (one 128-byte bank period per row) and d = 128 alike.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (D == 128) {
-    return ((row & 3) << 1) | (((row >> 2) & 1) << 3) | ((row >> 3) & 1);
-  } else {
-    return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
-  }
+  return ((row & 3) << 1) | ((row >> 2) & 1);
 }
 
 // Element offset of (row, col) in a swizzled [rows][D] tile.
@@ -125,37 +124,57 @@ __device__ __forceinline__ bf16x8 lds_read_col8_tr(const uint16_t* tile, int row
   return make_bf16x8((uint32_t)a[0], (uint32_t)a[1], (uint32_t)b[0], (uint32_t)b[1]);
 }
 
-// Cooperative copy of a ROWS x D bf16 tile (rows row0 .. row0 + ROWS - 1 of a [n_rows][D] head)
-// from global memory into registers, then into a swizzled LDS tile.  Rows at or past n_rows are
-// read from row n_rows - 1 instead (valid memory; the kernels mask those keys/queries).
+// Direct global -> LDS staging of a ROWS x D bf16 tile with buffer_load_dwordx4 ... lds: each
+// lane moves 16 bytes straight into LDS (lane l of a wave writes at the instruction's LDS base +
+// 16 l), so no registers hold the tile in flight.  The swizzle is applied on the global side:
+// LDS chunk position p (row p / (D/8), physical chunk p % (D/8)) is fed from logical chunk
+// physical ^ swz(row).  The buffer resource covers only rows row0 .. n_rows - 1 of the head, and
+// the hardware returns zeros for rows past it (the kernels mask those keys/queries anyway).
+// Completion is tracked by vmcnt: callers wait (wait_vm0) and then barrier before reading.
 template <int ROWS, int D, int NT>
-struct TileStage {
+struct DirectStage {
   static constexpr int kChunksPerRow = D / 8;
   static constexpr int kChunks = ROWS * kChunksPerRow;
-  static constexpr int kPer = kChunks / NT;
+  static constexpr int kWaves = NT / 64;
+  static constexpr int kPer = kChunks / NT;  // 16-byte loads per lane
   static_assert(kChunks % NT == 0, "tile must split evenly over the threads");
-  i32x4 buf[kPer];
+  int voff[kPer];  // byte offset of this lane's chunks relative to row0
+  int wave;
 
-  __device__ __forceinline__ void load(const uint16_t* head, int row0, int n_rows, int tid) {
+  __device__ __forceinline__ void init(int tid) {
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int ch = tid + i * NT;
-      const int r = ch / kChunksPerRow;
-      const int c = ch % kChunksPerRow;
-      const int gr = min(row0 + r, n_rows - 1);
-      buf[i] = *reinterpret_cast<const i32x4*>(head + (int64_t)gr * D + c * 8);
+      const int p = (wave * kPer + i) * 64 + l;
+      const int r = p / kChunksPerRow;
+      const int pc = p % kChunksPerRow;
+      voff[i] = r * (D * 2) + ((pc ^ swz<D>(r)) << 4);
     }
   }
-  __device__ __forceinline__ void store(uint16_t* tile, int tid) const {
+  __device__ __forceinline__ void issue(const uint16_t* head, int row0, int n_rows, uint16_t* tile) const {
+    // Device pass only: with the buffer-resource builtins visible to the host pass, clang drops
+    // the host launch stubs of all but one instantiation of the kernels that call this.
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int rows_left = n_rows - row0;
+    const int nbytes = rows_left > 0 ? rows_left * (D * 2) : 0;
+    __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(head + (int64_t)row0 * D), 0, nbytes, 0x00020000);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int ch = tid + i * NT;
-      const int r = ch / kChunksPerRow;
-      const int c = ch % kChunksPerRow;
-      *reinterpret_cast<i32x4*>(tile + r * D + ((c ^ swz<D>(r)) << 3)) = buf[i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)((char*)tile + (wave * kPer + i) * 1024), 16,
+          voff[i], 0, 0, 0);
     }
+#else
+    (void)head, (void)row0, (void)n_rows, (void)tile;
+#endif
   }
 };
+
+// Wait until this wave's outstanding vector-memory operations (including direct LDS loads) are
+// done: s_waitcnt vmcnt(0), other counters left at their maximum.
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Workgroup -> (head, tile rank).  The hardware hands consecutive workgroup ids to the 8 XCDs in
 // turn, so when the head count divides by 8, id x runs on XCD x % 8 and that XCD is given the

@@ -67,20 +67,19 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
   float lsum = 0.f;           // this half's share of the row sum
   int n_ones = 0;
 
-  TileStage<BC, D, kFwdThreads> stK, stV;
-  stK.load(Kg, 0, N, tid);
-  stV.load(Vg, 0, N, tid);
-  stK.store(sK[0], tid);
-  stV.store(sV[0], tid);
+  DirectStage<BC, D, kFwdThreads> st;
+  st.init(tid);
+  st.issue(Kg, 0, N, sK[0]);
+  st.issue(Vg, 0, N, sV[0]);
+  wait_vm0();
   __syncthreads();
 
   for (int j = 0; j < n_kv; ++j) {
     const int buf = j & 1;
     const int kv0 = j * BC;
-    const bool has_next = (j + 1 < n_kv);
-    if (has_next) {
-      stK.load(Kg, kv0 + BC, N, tid);
-      stV.load(Vg, kv0 + BC, N, tid);
+    if (j + 1 < n_kv) {
+      st.issue(Kg, kv0 + BC, N, sK[buf ^ 1]);
+      st.issue(Vg, kv0 + BC, N, sV[buf ^ 1]);
     }
     // A wave whose queries all precede this key block has nothing visible in it.
     const bool active = !CAUSAL || (kv0 <= qw0 + 31);
@@ -117,7 +116,9 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
         for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[kb][r]);
       tmax = halves_max(tmax);
       const float new_max = fmaxf(run_max, tmax);
-      if (COUNT) {
+      // The count can only change where the block reaches the running max; skip the whole
+      // count when no lane of the wave does (the common case once the max has settled).
+      if (COUNT && __any(tmax >= run_max)) {
         int tcnt = 0;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -171,10 +172,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
         }
       }
     }
-    if (has_next) {
-      stK.store(sK[buf ^ 1], tid);
-      stV.store(sV[buf ^ 1], tid);
-    }
+    wait_vm0();
     __syncthreads();
   }
 

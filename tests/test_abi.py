@@ -72,6 +72,7 @@ def test_forward_validation(lib, ffi):
     assert _fwd(lib, N=-5) == ffi.FA_ERR_SHAPE
     assert _fwd(lib, B=1 << 20, H=1 << 12) == ffi.FA_ERR_SHAPE
     assert _fwd(lib, N=1 << 30, H=1 << 10) == ffi.FA_ERR_SHAPE
+    assert _fwd(lib, N=(1 << 23), d=128, H=1) == ffi.FA_ERR_SHAPE  # one head over 2 GiB
     for d in (0, 32, 96, 256):
         assert _fwd(lib, d=d) == ffi.FA_ERR_HEADDIM
     for scale in (0.0, -1.0, float("nan"), float("inf")):
