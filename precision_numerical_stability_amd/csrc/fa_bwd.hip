@@ -10,6 +10,8 @@
 //
 // dK/dV and dQ run as two kernels with no atomics: each output tile is owned by exactly one
 // workgroup, so results are deterministic.  All three run on the caller's stream in order.
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -180,17 +182,121 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// dK/dV: one workgroup per (128-key tile, head), 4 waves of 32 keys; loops over 64-query blocks.
+// dK/dV: one workgroup per (128-key tile, head), 4 waves of 32 keys; loops over 128-query blocks.
 // S = Q K^T and dP = dO V^T put one key per lane (K and V stay in registers as B operands);
 // dV^T = dO^T P and dK^T = Q^T dS take P and dS from the accumulator registers, with dO^T and
 // Q^T read transposed from LDS.  The per-query LSE and delta come from LDS as 4-float vectors.
-// Each 32-query half of a block is finished before the next.
-constexpr int kDkvBq = 64;
+//
+// A block is processed as four 32-query sub-blocks in one straight-line software pipeline: the
+// S/dP products of sub-block t+1 are issued before the softmax-gradient arithmetic of sub-block t,
+// so the matrix cores work on the next sub-block while the vector ALUs finish the current one.
+constexpr int kDkvBq = 128;
 constexpr int kDkvBk = 128;
+
+template <int D>
+struct DkvFrags {
+  bf16x8 k[D / 16];
+  bf16x8 v[D / 16];
+};
+
+// S and dP for the 32 queries starting at tile row qr (one key per lane).
+template <int D>
+__device__ __forceinline__ void dkdv_sdp(const uint16_t* tQ, const uint16_t* tG, int qr, int l32, int hh,
+                                         const DkvFrags<D>& f, f32x16& s, f32x16& dp) {
+  s = zero16();
+  dp = zero16();
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const bf16x8 qa = lds_read_row8<D>(tQ, qr + l32, 16 * ks + 8 * hh);
+    const bf16x8 ga = lds_read_row8<D>(tG, qr + l32, 16 * ks + 8 * hh);
+    s = mfma32x32x16(qa, f.k[ks], s);
+    dp = mfma32x32x16(ga, f.v[ks], dp);
+  }
+}
+
+// P = exp2(S scale log2e - LSE log2e) and dS = P (dP - delta) for 32 queries, packed to bf16 in
+// the accumulator row order.  Queries past N or (causal) before this lane's key are masked.
+template <bool MASK, bool CAUSAL>
+__device__ __forceinline__ void dkdv_grad(const float* tL, const float* tD, int qr, int q0, int N, int key,
+                                          int hh, float sl2, const f32x16& s, const f32x16& dp,
+                                          uint32_t (&pp)[8], uint32_t (&pd)[8]) {
+#pragma unroll
+  for (int rq = 0; rq < 4; ++rq) {
+    const int qi = qr + 8 * rq + 4 * hh;
+    const float4 l4 = *reinterpret_cast<const float4*>(&tL[qi]);
+    const float4 d4 = *reinterpret_cast<const float4*>(&tD[qi]);
+    const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+    const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
+    float pv[4], dsv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = 4 * rq + u;
+      float p = fast_exp2(fmaf(s[r], sl2, -lv[u]));
+      if (MASK) {
+        const int qidx = q0 + qi + u;
+        const bool hide = (qidx >= N) || (CAUSAL && key > qidx);
+        p = hide ? 0.f : p;
+      }
+      pv[u] = p;
+      dsv[u] = p * (dp[r] - dl[u]);
+    }
+    pp[2 * rq] = pack_bf16x2(pv[0], pv[1]);
+    pp[2 * rq + 1] = pack_bf16x2(pv[2], pv[3]);
+    pd[2 * rq] = pack_bf16x2(dsv[0], dsv[1]);
+    pd[2 * rq + 1] = pack_bf16x2(dsv[2], dsv[3]);
+  }
+}
+
+// dV^T += dO^T P and dK^T += Q^T dS over the two 16-query slabs of one sub-block.
+template <int D>
+__device__ __forceinline__ void dkdv_accum(const uint16_t* tQ, const uint16_t* tG, int qr, int lane,
+                                           const uint32_t (&pp)[8], const uint32_t (&pd)[8],
+                                           f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int o4 = 4 * half;
+    const bf16x8 pb = make_bf16x8(pp[o4], pp[o4 + 1], pp[o4 + 2], pp[o4 + 3]);
+    const bf16x8 sb = make_bf16x8(pd[o4], pd[o4 + 1], pd[o4 + 2], pd[o4 + 3]);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const bf16x8 gt = lds_read_col8_tr<D>(tG, qr + 16 * half, 32 * dt, lane);
+      const bf16x8 qt = lds_read_col8_tr<D>(tQ, qr + 16 * half, 32 * dt, lane);
+      dv[dt] = mfma32x32x16(gt, pb, dv[dt]);
+      dk[dt] = mfma32x32x16(qt, sb, dk[dt]);
+    }
+  }
+}
+
+template <int D, bool CAUSAL, bool MASK>
+__device__ __forceinline__ void dkdv_block(const uint16_t* tQ, const uint16_t* tG, const float* tL,
+                                           const float* tD, int q0, int N, int key, int lane, float sl2,
+                                           const DkvFrags<D>& f, f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
+  constexpr int SB = kDkvBq / 32;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  f32x16 s, dp;
+  uint32_t pp[2][8], pd[2][8];
+  dkdv_sdp<D>(tQ, tG, 0, l32, hh, f, s, dp);
+  dkdv_grad<MASK, CAUSAL>(tL, tD, 0, q0, N, key, hh, sl2, s, dp, pp[0], pd[0]);
+#pragma unroll
+  for (int t = 1; t < SB; ++t) {
+    // S/dP of sub-block t, then its softmax-gradient arithmetic on the vector ALUs alongside the
+    // dV/dK products of sub-block t-1 on the matrix cores.  The fences keep the scheduler from
+    // hoisting operand reads across phases, which would exhaust the register file.
+    __builtin_amdgcn_sched_barrier(0);
+    dkdv_sdp<D>(tQ, tG, 32 * t, l32, hh, f, s, dp);
+    __builtin_amdgcn_sched_barrier(0);
+    dkdv_grad<MASK, CAUSAL>(tL, tD, 32 * t, q0, N, key, hh, sl2, s, dp, pp[t & 1], pd[t & 1]);
+    dkdv_accum<D>(tQ, tG, 32 * (t - 1), lane, pp[(t - 1) & 1], pd[(t - 1) & 1], dk, dv);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  dkdv_accum<D>(tQ, tG, 32 * (SB - 1), lane, pp[(SB - 1) & 1], pd[(SB - 1) & 1], dk, dv);
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
-  constexpr int BQ = kDkvBq, BK = kDkvBk, KS = D / 16, DT = D / 32, QB = BQ / 32;
+  constexpr int BQ = kDkvBq, BK = kDkvBk, KS = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BQ * D];
   __shared__ __attribute__((aligned(16))) uint16_t sG[2][BQ * D];
   __shared__ __attribute__((aligned(16))) float sL[2][BQ];
@@ -215,14 +321,14 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   const int key = kw0 + l32;
   const int ksrc = min(key, N - 1);
 
-  bf16x8 kf[KS], vf[KS];
+  DkvFrags<D> f;
   {
     const uint16_t* ks_ = a.k + hoff + (int64_t)ksrc * D + 8 * hh;
     const uint16_t* vs_ = a.v + hoff + (int64_t)ksrc * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = as_bf16x8(*reinterpret_cast<const i32x4*>(ks_ + 16 * ks));
-      vf[ks] = as_bf16x8(*reinterpret_cast<const i32x4*>(vs_ + 16 * ks));
+      f.k[ks] = as_bf16x8(*reinterpret_cast<const i32x4*>(ks_ + 16 * ks));
+      f.v[ks] = as_bf16x8(*reinterpret_cast<const i32x4*>(vs_ + 16 * ks));
     }
   }
 
@@ -253,17 +359,15 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
     }
   };
 
-  if (i_first < n_q) {
-    st.issue(Qg, i_first * BQ, N, sQ[0]);
-    st.issue(Gg, i_first * BQ, N, sG[0]);
-    load_rows(i_first);
-    store_rows(0);
-  }
-  wait_vm0();
-  __syncthreads();
-
-  for (int i = i_first; i < n_q; ++i) {
-    const int buf = (i - i_first) & 1;
+  // Blocks are visited in order i_first .. n_q - 1.  Only two of them can need masking: the
+  // causal diagonal block (the first, since key and query tiles have the same height) and a
+  // ragged last block.  They run through the masked body outside the main loop, so the loop body
+  // has a single variant and the accumulators need no copies at branch joins.
+  static_assert(kDkvBq == kDkvBk, "the diagonal block must be the first block");
+  int i = i_first;
+  int buf = 0;
+  auto step = [&](auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int q0 = i * BQ;
     const bool has_next = (i + 1 < n_q);
     if (has_next) {
@@ -271,69 +375,28 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
       st.issue(Gg, q0 + BQ, N, sG[buf ^ 1]);
       load_rows(i + 1);
     }
-    // A wave whose keys all follow every query of this block sees nothing in it.
-    const bool active = !CAUSAL || (q0 + BQ - 1 >= kw0);
-    if (active) {
-      const uint16_t* tQ = sQ[buf];
-      const uint16_t* tG = sG[buf];
-      const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (q0 + BQ > N);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 qa = lds_read_row8<D>(tQ, 32 * qb + l32, 16 * ks + 8 * hh);
-          const bf16x8 ga = lds_read_row8<D>(tG, 32 * qb + l32, 16 * ks + 8 * hh);
-          s = mfma32x32x16(qa, kf[ks], s);
-          dp = mfma32x32x16(ga, vf[ks], dp);
-        }
-        // Rows of s/dp here are queries 32 qb + 8 (r/4) + 4 hh + (r%4); column = this lane's key.
-        uint32_t pp[8], pd[8];
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int qi = 32 * qb + 8 * rq + 4 * hh;
-          const float4 l4 = *reinterpret_cast<const float4*>(&sL[buf][qi]);
-          const float4 d4 = *reinterpret_cast<const float4*>(&sD[buf][qi]);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-          float pv[4], dsv[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int r = 4 * rq + u;
-            float p = fast_exp2(fmaf(s[r], a.sl2, -lv[u]));
-            if (need_mask) {
-              const int qidx = q0 + qi + u;
-              const bool hide = (qidx >= N) || (CAUSAL && key > qidx);
-              p = hide ? 0.f : p;
-            }
-            pv[u] = p;
-            dsv[u] = p * (dp[r] - dv4[u]);
-          }
-          pp[2 * rq] = pack_bf16x2(pv[0], pv[1]);
-          pp[2 * rq + 1] = pack_bf16x2(pv[2], pv[3]);
-          pd[2 * rq] = pack_bf16x2(dsv[0], dsv[1]);
-          pd[2 * rq + 1] = pack_bf16x2(dsv[2], dsv[3]);
-        }
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int kk = 2 * qb + half;
-          const int o4 = 4 * half;
-          const bf16x8 pb = make_bf16x8(pp[o4], pp[o4 + 1], pp[o4 + 2], pp[o4 + 3]);
-          const bf16x8 sb = make_bf16x8(pd[o4], pd[o4 + 1], pd[o4 + 2], pd[o4 + 3]);
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const bf16x8 gt = lds_read_col8_tr<D>(tG, 16 * kk, 32 * dt, lane);
-            const bf16x8 qt = lds_read_col8_tr<D>(tQ, 16 * kk, 32 * dt, lane);
-            dv[dt] = mfma32x32x16(gt, pb, dv[dt]);
-            dk[dt] = mfma32x32x16(qt, sb, dk[dt]);
-          }
-        }
-      }
-    }
+    dkdv_block<D, CAUSAL, MASK>(sQ[buf], sG[buf], sL[buf], sD[buf], q0, N, key, lane, a.sl2, f, dk, dv);
     if (has_next) store_rows(buf ^ 1);
     wait_vm0();
     __syncthreads();
+    ++i;
+    buf ^= 1;
+  };
+  using masked = std::integral_constant<bool, true>;
+  using plain = std::integral_constant<bool, false>;
+
+  if (i < n_q) {
+    st.issue(Qg, i * BQ, N, sQ[0]);
+    st.issue(Gg, i * BQ, N, sG[0]);
+    load_rows(i);
+    store_rows(0);
   }
+  wait_vm0();
+  __syncthreads();
+  const int n_full = N / BQ;  // blocks lying entirely inside the sequence
+  if (CAUSAL && i < n_q) step(masked{});
+  while (i < n_full) step(plain{});
+  if (i < n_q) step(masked{});
 
   if (key < N) {
     uint16_t* dkr = a.dk + hoff + (int64_t)key * D;
