@@ -54,15 +54,67 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------------------------
 // dQ: one workgroup per (128-query tile, head), 4 waves of 32 queries; loops over 64-key blocks.
 // Lane layout as in the forward: S^T = K Q^T and dP^T = V dO^T put one query per lane, so LSE
-// and delta are lane-local; dQ^T = K^T dS^T takes dS^T from the accumulator registers.  Each
-// 32-key half of a block is finished (S, dP, dS, its dQ products) before the next, which keeps
-// only one half's scores in registers.
+// and delta are lane-local; dQ^T = K^T dS^T takes dS^T from the accumulator registers.  Within a
+// block, the S/dP products of the second 32-key half are issued before the dS arithmetic of the
+// first half and the dQ products follow, so matrix and vector work can overlap.  Blocks that need
+// a mask (causal diagonal, ragged tail) run through the masked body after the main loop.
 constexpr int kDqBc = 64;
 constexpr int kDqBr = 128;
 
+template <int D>
+__device__ __forceinline__ void dq_sdp(const uint16_t* tK, const uint16_t* tV, int kr, int l32, int hh,
+                                       const bf16x8 (&qf)[D / 16], const bf16x8 (&gf)[D / 16], f32x16& s,
+                                       f32x16& dp) {
+  s = zero16();
+  dp = zero16();
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const bf16x8 kf = lds_read_row8<D>(tK, kr + l32, 16 * ks + 8 * hh);
+    const bf16x8 vf = lds_read_row8<D>(tV, kr + l32, 16 * ks + 8 * hh);
+    s = mfma32x32x16(kf, qf[ks], s);
+    dp = mfma32x32x16(vf, gf[ks], dp);
+  }
+}
+
+template <bool MASK, bool CAUSAL>
+__device__ __forceinline__ void dq_grad(const f32x16& s, const f32x16& dp, int key0, int qrow, int N, int hh,
+                                        float sl2, float lse2, float dlt, uint32_t (&pds)[8]) {
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    float ds2[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int rr = r + u;
+      float p = fast_exp2(fmaf(s[rr], sl2, -lse2));
+      if (MASK) {
+        const int key = key0 + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+        const bool hide = (key >= N) || (CAUSAL && key > qrow);
+        p = hide ? 0.f : p;
+      }
+      ds2[u] = p * (dp[rr] - dlt);
+    }
+    pds[r >> 1] = pack_bf16x2(ds2[0], ds2[1]);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void dq_accum(const uint16_t* tK, int kr, int lane, const uint32_t (&pds)[8],
+                                         f32x16 (&acc)[D / 32]) {
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const bf16x8 db = make_bf16x8(pds[4 * half], pds[4 * half + 1], pds[4 * half + 2], pds[4 * half + 3]);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const bf16x8 kt = lds_read_col8_tr<D>(tK, kr + 16 * half, 32 * dt, lane);
+      acc[dt] = mfma32x32x16(kt, db, acc[dt]);
+    }
+  }
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
-  constexpr int BC = kDqBc, BR = kDqBr, KS = D / 16, DT = D / 32, KB = BC / 32;
+  constexpr int BC = kDqBc, BR = kDqBr, KS = D / 16, DT = D / 32;
+  static_assert(BC == 64, "the block body handles two 32-key halves");
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BC * D];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][BC * D];
 
@@ -80,8 +132,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
   const int64_t hoff = (int64_t)bh * N * D;
   const uint16_t* Kg = a.k + hoff;
   const uint16_t* Vg = a.v + hoff;
-  const int qw0 = q0 + wave * 32;
-  const int qrow = qw0 + l32;
+  const int qrow = q0 + wave * 32 + l32;
   const int qsrc = min(qrow, N - 1);
 
   bf16x8 qf[KS], gf[KS];
@@ -99,6 +150,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
 
   int n_kv = (N + BC - 1) / BC;
   if (CAUSAL) n_kv = min(n_kv, (q0 + BR - 1) / BC + 1);
+  const int n_plain = min(n_kv, CAUSAL ? q0 / BC : N / BC);
 
   f32x16 acc[DT];
 #pragma unroll
@@ -111,60 +163,37 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
   wait_vm0();
   __syncthreads();
 
-  for (int j = 0; j < n_kv; ++j) {
+  int j = 0;
+  auto step = [&](auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int buf = j & 1;
     const int kv0 = j * BC;
     if (j + 1 < n_kv) {
       st.issue(Kg, kv0 + BC, N, sK[buf ^ 1]);
       st.issue(Vg, kv0 + BC, N, sV[buf ^ 1]);
     }
-    const bool active = !CAUSAL || (kv0 <= qw0 + 31);
-    if (active) {
-      const uint16_t* tK = sK[buf];
-      const uint16_t* tV = sV[buf];
-      const bool need_mask = CAUSAL ? (kv0 + BC - 1 > qw0) : (kv0 + BC > N);
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 kf = lds_read_row8<D>(tK, 32 * kb + l32, 16 * ks + 8 * hh);
-          const bf16x8 vf = lds_read_row8<D>(tV, 32 * kb + l32, 16 * ks + 8 * hh);
-          s = mfma32x32x16(kf, qf[ks], s);
-          dp = mfma32x32x16(vf, gf[ks], dp);
-        }
-        uint32_t pds[8];
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          float ds2[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int rr = r + u;
-            float p = fast_exp2(fmaf(s[rr], a.sl2, -lse2));
-            if (need_mask) {
-              const int key = kv0 + 32 * kb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-              const bool hide = (key >= N) || (CAUSAL && key > qrow);
-              p = hide ? 0.f : p;
-            }
-            ds2[u] = p * (dp[rr] - dlt);
-          }
-          pds[r >> 1] = pack_bf16x2(ds2[0], ds2[1]);
-        }
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int kk = 2 * kb + half;
-          const bf16x8 db = make_bf16x8(pds[4 * half], pds[4 * half + 1], pds[4 * half + 2], pds[4 * half + 3]);
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const bf16x8 kt = lds_read_col8_tr<D>(tK, 16 * kk, 32 * dt, lane);
-            acc[dt] = mfma32x32x16(kt, db, acc[dt]);
-          }
-        }
-      }
-    }
+    const uint16_t* tK = sK[buf];
+    const uint16_t* tV = sV[buf];
+    f32x16 s, dp;
+    uint32_t pds0[8], pds1[8];
+    __builtin_amdgcn_sched_barrier(0);
+    dq_sdp<D>(tK, tV, 0, l32, hh, qf, gf, s, dp);
+    __builtin_amdgcn_sched_barrier(0);
+    dq_grad<MASK, CAUSAL>(s, dp, kv0, qrow, N, hh, a.sl2, lse2, dlt, pds0);
+    __builtin_amdgcn_sched_barrier(0);
+    dq_sdp<D>(tK, tV, 32, l32, hh, qf, gf, s, dp);
+    __builtin_amdgcn_sched_barrier(0);
+    dq_grad<MASK, CAUSAL>(s, dp, kv0 + 32, qrow, N, hh, a.sl2, lse2, dlt, pds1);
+    dq_accum<D>(tK, 0, lane, pds0, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    dq_accum<D>(tK, 32, lane, pds1, acc);
+    __builtin_amdgcn_sched_barrier(0);
     wait_vm0();
     __syncthreads();
-  }
+    ++j;
+  };
+  while (j < n_plain) step(std::integral_constant<bool, false>{});
+  while (j < n_kv) step(std::integral_constant<bool, true>{});
 
   if (qrow < N) {
     uint16_t* dst = a.dq + hoff + (int64_t)qrow * D;

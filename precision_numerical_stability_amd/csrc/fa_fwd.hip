@@ -12,6 +12,8 @@
 // of 64 keys are staged through swizzled, double-buffered LDS; Q stays in registers.  O^T is
 // accumulated as V^T P^T so that the per-query rescale factor is lane-local too, and P^ goes from
 // the accumulator registers straight into the next MFMA's operand without touching LDS.
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -44,8 +46,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
   const uint16_t* Kg = a.k + hoff;
   const uint16_t* Vg = a.v + hoff;
 
-  const int qw0 = q0 + wave * 32;  // first query of this wave
-  const int qrow = qw0 + l32;      // this lane's query
+  const int qrow = q0 + wave * 32 + l32;  // this lane's query
 
   // Q^T as the B operand: lane holds Q[qrow][16 ks + 8 hh .. + 7].
   bf16x8 qf[KS];
@@ -74,107 +75,114 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
   wait_vm0();
   __syncthreads();
 
-  for (int j = 0; j < n_kv; ++j) {
+  // Leading blocks visible to every query of the tile need no mask; the rest (causal diagonal,
+  // ragged tail) run through the masked body after the main loop, so the loop body has a single
+  // variant.
+  const int n_plain = min(n_kv, CAUSAL ? q0 / BC : N / BC);
+  int j = 0;
+  auto step = [&](auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int buf = j & 1;
     const int kv0 = j * BC;
     if (j + 1 < n_kv) {
       st.issue(Kg, kv0 + BC, N, sK[buf ^ 1]);
       st.issue(Vg, kv0 + BC, N, sV[buf ^ 1]);
     }
-    // A wave whose queries all precede this key block has nothing visible in it.
-    const bool active = !CAUSAL || (kv0 <= qw0 + 31);
-    if (active) {
-      const uint16_t* tK = sK[buf];
-      const uint16_t* tV = sV[buf];
-      // S^T block kb: rows = keys kv0 + 32 kb + (8 (r/4) + 4 hh + r%4), column = this lane's query.
-      f32x16 s[KB];
+    const uint16_t* tK = sK[buf];
+    const uint16_t* tV = sV[buf];
+    // S^T block kb: rows = keys kv0 + 32 kb + (8 (r/4) + 4 hh + r%4), column = this lane's query.
+    f32x16 s[KB];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        s[kb] = zero16();
+    for (int kb = 0; kb < KB; ++kb) {
+      s[kb] = zero16();
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          bf16x8 kf = lds_read_row8<D>(tK, 32 * kb + l32, 16 * ks + 8 * hh);
-          s[kb] = mfma32x32x16(kf, qf[ks], s[kb]);
-        }
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 kf = lds_read_row8<D>(tK, 32 * kb + l32, 16 * ks + 8 * hh);
+        s[kb] = mfma32x32x16(kf, qf[ks], s[kb]);
       }
-      const bool need_mask = CAUSAL ? (kv0 + BC - 1 > qw0) : (kv0 + BC > N);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool hide = (key >= N) || (CAUSAL && key > qrow);
-            s[kb][r] = hide ? -INFINITY : s[kb][r];
-          }
-      }
-      // Block max over both halves, and (when needed) how many visible keys attain it.
-      float tmax = -INFINITY;
+    }
+    if (MASK) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[kb][r]);
-      tmax = halves_max(tmax);
-      const float new_max = fmaxf(run_max, tmax);
-      // The count can only change where the block reaches the running max; skip the whole
-      // count when no lane of the wave does (the common case once the max has settled).
-      if (COUNT && __any(tmax >= run_max)) {
-        int tcnt = 0;
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const bool hide = (key >= N) || (CAUSAL && key > qrow);
+          s[kb][r] = hide ? -INFINITY : s[kb][r];
+        }
+    }
+    // Block max over both halves, and (when needed) how many visible keys attain it.
+    float tmax = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) tcnt += (s[kb][r] == tmax) ? 1 : 0;
-        tcnt = halves_sum_i(tcnt);
-        if (tmax == -INFINITY) tcnt = 0;
-        run_cnt = ((tmax == new_max) ? tcnt : 0) + ((run_max == new_max) ? run_cnt : 0);
-      }
-      run_max = new_max;
-      // Shift for this block (log2 units).  The sign test is unchanged by the positive factor
-      // scale * log2(e), and the rule is positively homogeneous, so applying it here equals
-      // applying it to the natural-log scores.
-      const float r2 = run_max * a.sl2;
-      float m2_new = r2;
-      if (MODE != 0) {
-        const bool rep = (MODE == 2) || (run_cnt > 1);
-        m2_new = (rep && r2 > 0.f) ? a.beta * r2 : ((rep && r2 < 0.f) ? 0.f : r2);
-      }
-      const float alpha = fast_exp2(m2 - m2_new);
-      m2 = m2_new;
-      // P^ = exp2(S * scale * log2e - m), its row sum, and its bf16 packing for the V product.
-      uint32_t pk[KB][8];
-      float psum = 0.f;
+      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[kb][r]);
+    tmax = halves_max(tmax);
+    const float new_max = fmaxf(run_max, tmax);
+    // The count can only change where the block reaches the running max; skip the whole count
+    // when no lane of the wave does (the common case once the max has settled).
+    if (COUNT && __any(tmax >= run_max)) {
+      int tcnt = 0;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(fmaf(s[kb][r], a.sl2, -m2_new));
-          const float p1 = fast_exp2(fmaf(s[kb][r + 1], a.sl2, -m2_new));
-          psum += p0 + p1;
-          const uint32_t w = pack_bf16x2(p0, p1);
-          pk[kb][r >> 1] = w;
-          if (STATS) n_ones += ((w & 0xFFFFu) == kBf16One) + ((w >> 16) == kBf16One);
-        }
-      lsum = alpha * lsum + psum;
+        for (int r = 0; r < 16; ++r) tcnt += (s[kb][r] == tmax) ? 1 : 0;
+      tcnt = halves_sum_i(tcnt);
+      if (tmax == -INFINITY) tcnt = 0;
+      run_cnt = ((tmax == new_max) ? tcnt : 0) + ((run_max == new_max) ? run_cnt : 0);
+    }
+    run_max = new_max;
+    // Shift for this block (log2 units).  The sign test is unchanged by the positive factor
+    // scale * log2(e), and the rule is positively homogeneous, so applying it here equals
+    // applying it to the natural-log scores.
+    const float r2 = run_max * a.sl2;
+    float m2_new = r2;
+    if (MODE != 0) {
+      const bool rep = (MODE == 2) || (run_cnt > 1);
+      m2_new = (rep && r2 > 0.f) ? a.beta * r2 : ((rep && r2 < 0.f) ? 0.f : r2);
+    }
+    const float alpha = fast_exp2(m2 - m2_new);
+    m2 = m2_new;
+    // P^ = exp2(S * scale * log2e - m), its row sum, and its bf16 packing for the V product.
+    uint32_t pk[KB][8];
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = fast_exp2(fmaf(s[kb][r], a.sl2, -m2_new));
+        const float p1 = fast_exp2(fmaf(s[kb][r + 1], a.sl2, -m2_new));
+        psum += p0 + p1;
+        const uint32_t w = pack_bf16x2(p0, p1);
+        pk[kb][r >> 1] = w;
+        if (STATS) n_ones += ((w & 0xFFFFu) == kBf16One) + ((w >> 16) == kBf16One);
+      }
+    lsum = alpha * lsum + psum;
+    // Rescale O only if some lane's shift moved (alpha == 1 exactly leaves O unchanged).
+    if (__any(alpha != 1.f)) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-      // O^T += V^T P^T over 16-key slabs.
+    }
+    // O^T += V^T P^T over 16-key slabs.
 #pragma unroll
-      for (int kk = 0; kk < BC / 16; ++kk) {
-        const int kb = kk >> 1;
-        const int o4 = (kk & 1) * 4;
-        const bf16x8 pb = make_bf16x8(pk[kb][o4], pk[kb][o4 + 1], pk[kb][o4 + 2], pk[kb][o4 + 3]);
+    for (int kk = 0; kk < BC / 16; ++kk) {
+      const int kb = kk >> 1;
+      const int o4 = (kk & 1) * 4;
+      const bf16x8 pb = make_bf16x8(pk[kb][o4], pk[kb][o4 + 1], pk[kb][o4 + 2], pk[kb][o4 + 3]);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const bf16x8 vf = lds_read_col8_tr<D>(tV, 16 * kk, 32 * dt, lane);
-          oacc[dt] = mfma32x32x16(vf, pb, oacc[dt]);
-        }
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 vf = lds_read_col8_tr<D>(tV, 16 * kk, 32 * dt, lane);
+        oacc[dt] = mfma32x32x16(vf, pb, oacc[dt]);
       }
     }
     wait_vm0();
     __syncthreads();
-  }
+    ++j;
+  };
+  while (j < n_plain) step(std::integral_constant<bool, false>{});
+  while (j < n_kv) step(std::integral_constant<bool, true>{});
 
   // Epilogue: O = O^T / l, LSE = m + ln l, diagnostics.
   const float ltot = halves_sum(lsum);
