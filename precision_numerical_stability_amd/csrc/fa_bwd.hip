@@ -176,17 +176,22 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
     const uint16_t* tV = sV[buf];
     f32x16 s, dp;
     uint32_t pds0[8], pds1[8];
+    f32x16 s1, dp1;
     __builtin_amdgcn_sched_barrier(0);
     dq_sdp<D>(tK, tV, 0, l32, hh, qf, gf, s, dp);
+    sched_reads_ahead<2 * KS, 1, 4>();
     __builtin_amdgcn_sched_barrier(0);
+    // dS of the first half on the vector ALUs while the second half's S/dP run on the matrix cores.
+    dq_sdp<D>(tK, tV, 32, l32, hh, qf, gf, s1, dp1);
     dq_grad<MASK, CAUSAL>(s, dp, kv0, qrow, N, hh, a.sl2, lse2, dlt, pds0);
+    sched_reads_ahead_valu<2 * KS, 1, 4, 4>();
     __builtin_amdgcn_sched_barrier(0);
-    dq_sdp<D>(tK, tV, 32, l32, hh, qf, gf, s, dp);
-    __builtin_amdgcn_sched_barrier(0);
-    dq_grad<MASK, CAUSAL>(s, dp, kv0 + 32, qrow, N, hh, a.sl2, lse2, dlt, pds1);
+    dq_grad<MASK, CAUSAL>(s1, dp1, kv0 + 32, qrow, N, hh, a.sl2, lse2, dlt, pds1);
     dq_accum<D>(tK, 0, lane, pds0, acc);
+    sched_reads_ahead_valu<2 * DT, 2, 3, 8>();
     __builtin_amdgcn_sched_barrier(0);
     dq_accum<D>(tK, 32, lane, pds1, acc);
+    sched_reads_ahead<2 * DT, 2, 3>();
     __builtin_amdgcn_sched_barrier(0);
     wait_vm0();
     __syncthreads();
@@ -245,12 +250,12 @@ __device__ __forceinline__ void dkdv_sdp(const uint16_t* tQ, const uint16_t* tG,
 
 // P = exp2(S scale log2e - LSE log2e) and dS = P (dP - delta) for 32 queries, packed to bf16 in
 // the accumulator row order.  Queries past N or (causal) before this lane's key are masked.
-template <bool MASK, bool CAUSAL>
+template <bool MASK, bool CAUSAL, int RQ0 = 0, int RQ1 = 4>
 __device__ __forceinline__ void dkdv_grad(const float* tL, const float* tD, int qr, int q0, int N, int key,
                                           int hh, float sl2, const f32x16& s, const f32x16& dp,
                                           uint32_t (&pp)[8], uint32_t (&pd)[8]) {
 #pragma unroll
-  for (int rq = 0; rq < 4; ++rq) {
+  for (int rq = RQ0; rq < RQ1; ++rq) {
     const int qi = qr + 8 * rq + 4 * hh;
     const float4 l4 = *reinterpret_cast<const float4*>(&tL[qi]);
     const float4 d4 = *reinterpret_cast<const float4*>(&tD[qi]);
@@ -296,30 +301,48 @@ __device__ __forceinline__ void dkdv_accum(const uint16_t* tQ, const uint16_t* t
   }
 }
 
+// Software pipeline over the sub-blocks of one block.  The softmax-gradient arithmetic of a
+// sub-block is split in two halves (accumulator rows 0-7 and 8-15 of each 16-row group, i.e. the
+// two 16-query slabs), so that every phase pairs matrix work with vector work:
+//   P1(t): S/dP of sub-block t+1 (MFMA)  with  second half of grad(t) (VALU)
+//   P2(t): dV/dK of sub-block t  (MFMA)  with  first half of grad(t+1) (VALU)
+// S/dP and the packed P/dS are double-buffered across sub-blocks.
 template <int D, bool CAUSAL, bool MASK>
 __device__ __forceinline__ void dkdv_block(const uint16_t* tQ, const uint16_t* tG, const float* tL,
                                            const float* tD, int q0, int N, int key, int lane, float sl2,
                                            const DkvFrags<D>& f, f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
   constexpr int SB = kDkvBq / 32;
+  constexpr int KSN = 2 * (D / 16);  // S/dP MFMAs per sub-block
+  constexpr int ACN = 4 * (D / 32);  // dV/dK MFMAs per sub-block
   const int l32 = lane & 31;
   const int hh = lane >> 5;
-  f32x16 s, dp;
+  f32x16 s[2], dp[2];
   uint32_t pp[2][8], pd[2][8];
-  dkdv_sdp<D>(tQ, tG, 0, l32, hh, f, s, dp);
-  dkdv_grad<MASK, CAUSAL>(tL, tD, 0, q0, N, key, hh, sl2, s, dp, pp[0], pd[0]);
-#pragma unroll
-  for (int t = 1; t < SB; ++t) {
-    // S/dP of sub-block t, then its softmax-gradient arithmetic on the vector ALUs alongside the
-    // dV/dK products of sub-block t-1 on the matrix cores.  The fences keep the scheduler from
-    // hoisting operand reads across phases, which would exhaust the register file.
-    __builtin_amdgcn_sched_barrier(0);
-    dkdv_sdp<D>(tQ, tG, 32 * t, l32, hh, f, s, dp);
-    __builtin_amdgcn_sched_barrier(0);
-    dkdv_grad<MASK, CAUSAL>(tL, tD, 32 * t, q0, N, key, hh, sl2, s, dp, pp[t & 1], pd[t & 1]);
-    dkdv_accum<D>(tQ, tG, 32 * (t - 1), lane, pp[(t - 1) & 1], pd[(t - 1) & 1], dk, dv);
-  }
   __builtin_amdgcn_sched_barrier(0);
-  dkdv_accum<D>(tQ, tG, 32 * (SB - 1), lane, pp[(SB - 1) & 1], pd[(SB - 1) & 1], dk, dv);
+  dkdv_sdp<D>(tQ, tG, 0, l32, hh, f, s[0], dp[0]);
+  sched_reads_ahead<KSN, 1, 4>();
+  __builtin_amdgcn_sched_barrier(0);
+  dkdv_grad<MASK, CAUSAL, 0, 2>(tL, tD, 0, q0, N, key, hh, sl2, s[0], dp[0], pp[0], pd[0]);
+#pragma unroll
+  for (int t = 0; t < SB; ++t) {
+    const int c = t & 1, n = c ^ 1;
+    __builtin_amdgcn_sched_barrier(0);
+    if (t + 1 < SB) {
+      dkdv_sdp<D>(tQ, tG, 32 * (t + 1), l32, hh, f, s[n], dp[n]);
+      dkdv_grad<MASK, CAUSAL, 2, 4>(tL, tD, 32 * t, q0, N, key, hh, sl2, s[c], dp[c], pp[c], pd[c]);
+      sched_reads_ahead_valu<KSN, 1, 4, 6>();
+    } else {
+      dkdv_grad<MASK, CAUSAL, 2, 4>(tL, tD, 32 * t, q0, N, key, hh, sl2, s[c], dp[c], pp[c], pd[c]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    dkdv_accum<D>(tQ, tG, 32 * t, lane, pp[c], pd[c], dk, dv);
+    if (t + 1 < SB) {
+      dkdv_grad<MASK, CAUSAL, 0, 2>(tL, tD, 32 * (t + 1), q0, N, key, hh, sl2, s[n], dp[n], pp[n], pd[n]);
+      sched_reads_ahead_valu<ACN, 2, 3, 6>();
+    } else {
+      sched_reads_ahead<ACN, 2, 3>();
+    }
+  }
   __builtin_amdgcn_sched_barrier(0);
 }
 

@@ -83,15 +83,24 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // ---------------------------------------------------------------------------------------------
 // Swizzled row-major [rows][D] bf16 tiles in LDS.  The 16-byte chunk c of row r is stored at
-// chunk c ^ f(r), f(r) = 2 (r mod 4) + (r / 4) mod 2.  With 32 four-byte banks (128 bytes per
-// cycle), a 16-byte operand read serves 8 lanes per cycle -- 8 consecutive rows at the same
-// logical chunk -- and f(r) mod 8 is distinct over any 8 consecutive rows; a transpose read
-// serves one 16-lane group per cycle -- 4 consecutive rows (aligned to 4) at an aligned chunk
-// pair -- and f(r) / 2 is distinct over those 4 rows.  Both patterns are therefore free of bank
-// conflicts, for d = 64 (one 128-byte bank period per row) and d = 128 alike.
+// chunk c ^ f(r), with f an XOR-linear map of the low four bits r0..r3 of the row:
+//   d = 128 (16 chunks per row):  f = 4 r0 ^ 10 r1 ^ 1 r2 ^ 8 r3
+//   d = 64  ( 8 chunks per row):  f = 2 r0 ^  4 r1 ^ 1 r2 ^ 2 r3
+// The two access patterns are 16-byte operand reads (lanes = consecutive rows at one logical
+// chunk) and transpose reads (16-lane groups = 4 consecutive rows at an aligned chunk pair, the
+// two groups of a half-wave side by side).  These maps were chosen by exhaustive search over
+// XOR-linear maps so that both patterns are free of bank conflicts whether the LDS serves
+// 128 bytes per cycle (32 banks: 8 / 16 lanes per cycle) or 256 bytes (64 banks: 16 / 32 lanes);
+// the counters on gfx950 rule out a 32-bank-only design (a map conflict-free only for 32 banks
+// doubled the measured conflict cycles).
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  return ((row & 3) << 1) | ((row >> 2) & 1);
+  const int r0 = row & 1, r1 = (row >> 1) & 1, r2 = (row >> 2) & 1, r3 = (row >> 3) & 1;
+  if constexpr (D == 128) {
+    return (r0 << 2) ^ (r1 * 10) ^ r2 ^ (r3 << 3);
+  } else {
+    return (r0 << 1) ^ (r1 << 2) ^ r2 ^ (r3 << 1);
+  }
 }
 
 // Element offset of (row, col) in a swizzled [rows][D] tile.
@@ -171,6 +180,38 @@ struct DirectStage {
 #endif
   }
 };
+
+// Scheduling-group masks for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedDsRead = 0x100;
+
+// Ask the scheduler to run LDS operand reads DEPTH MFMAs ahead of the MFMAs that consume them:
+// DEPTH reads first, then (MFMA, READS_PER reads) pairs, then the remaining MFMAs.  Applies to
+// the scheduling region the call sits in (between sched_barrier fences).
+template <int N_MFMA, int READS_PER, int DEPTH>
+__device__ __forceinline__ void sched_reads_ahead() {
+#pragma unroll
+  for (int i = 0; i < DEPTH * READS_PER; ++i) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+#pragma unroll
+  for (int i = 0; i < N_MFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if (i + DEPTH < N_MFMA) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, READS_PER, 0);
+  }
+}
+
+// As sched_reads_ahead, with VALU_PER vector instructions placed after each MFMA as well.
+template <int N_MFMA, int READS_PER, int DEPTH, int VALU_PER>
+__device__ __forceinline__ void sched_reads_ahead_valu() {
+#pragma unroll
+  for (int i = 0; i < DEPTH * READS_PER; ++i) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+#pragma unroll
+  for (int i = 0; i < N_MFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if (i + DEPTH < N_MFMA) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, READS_PER, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, VALU_PER, 0);
+  }
+}
 
 // Wait until this wave's outstanding vector-memory operations (including direct LDS loads) are
 // done: s_waitcnt vmcnt(0), other counters left at their maximum.

@@ -6,12 +6,22 @@
 // 训练稳定性优化实践" (jsqmd.com/news/761560) §3.2: Q K^T accumulated in fp32, softmax in fp32,
 // P^ rounded to bf16 for the product with V.
 //
-// Work split: one workgroup of 4 waves per (query tile of 128 rows, head).  Each wave owns 32
+// Work split: one workgroup of 8 waves per (query tile of 256 rows, head).  Each wave owns 32
 // queries and computes S^T = K Q^T, so each lane owns one query column: its row max, repeat count
-// and row sum are lane-local up to one exchange between the two 32-lane halves.  K and V tiles
-// of 64 keys are staged through swizzled, double-buffered LDS; Q stays in registers.  O^T is
+// and row sum are lane-local up to one exchange between the two 32-lane halves.  O^T is
 // accumulated as V^T P^T so that the per-query rescale factor is lane-local too, and P^ goes from
 // the accumulator registers straight into the next MFMA's operand without touching LDS.
+//
+// Ping-pong: on gfx950 a wave overlaps only a few vector instructions with its own matrix
+// instructions, but two waves on one SIMD overlap almost completely when one issues MFMAs and the
+// other vector work.  The 8 waves form two groups (waves 0-3 and 4-7, one of each per SIMD) that
+// run in alternate phases separated by workgroup barriers:
+//   matrix phase M(j): O += V^T P^T of block j-1, then S^T of block j     (MFMA)
+//   vector phase V(j): mask, max/count/shift, P^ of block j, rescale O    (VALU)
+// Group A runs M(0) V(0) M(1) V(1) ...; group B runs one phase behind, so in every phase one group
+// works on the matrix cores while the other works on the vector ALUs.  K and V blocks of 64 keys
+// are double-buffered in LDS: K_{j+1} and V_j are loaded during phase 2j; K_j is read in phases
+// 2j (A) and 2j+1 (B), V_j in phases 2j+2 (A) and 2j+3 (B).
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -19,12 +29,21 @@
 
 namespace fa {
 
-constexpr int kFwdBc = 64;   // keys per step
-constexpr int kFwdBr = 128;  // queries per workgroup
-constexpr int kFwdThreads = 256;
+constexpr int kFwdBc = 64;   // keys per block
+constexpr int kFwdBr = 256;  // queries per workgroup
+constexpr int kFwdThreads = 512;
+
+// Per-lane running state of the online softmax for one query (this lane's column).
+struct RowState {
+  float run_max;  // running max of the raw dot products q.k
+  int run_cnt;    // how many visible keys attain it
+  float m2;       // current shift, in log2 units of the scaled score
+  float lsum;     // this half-wave's share of the row sum
+  int n_ones;     // exact-1.0 bf16 P^ values seen (stats variant)
+};
 
 template <int D, bool CAUSAL, int MODE, bool STATS>
-__global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   constexpr int BC = kFwdBc, BR = kFwdBr, KS = D / 16, DT = D / 32, KB = BC / 32;
   constexpr bool COUNT = (MODE == 1) || STATS;
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BC * D];
@@ -32,7 +51,8 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // 0: leads, 1: one phase behind
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
@@ -46,7 +66,8 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
   const uint16_t* Kg = a.k + hoff;
   const uint16_t* Vg = a.v + hoff;
 
-  const int qrow = q0 + wave * 32 + l32;  // this lane's query
+  const int qw0 = q0 + wave * 32;  // first query of this wave
+  const int qrow = qw0 + l32;      // this lane's query
 
   // Q^T as the B operand: lane holds Q[qrow][16 ks + 8 hh .. + 7].
   bf16x8 qf[KS];
@@ -58,50 +79,79 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
 
   int n_kv = (N + BC - 1) / BC;
   if (CAUSAL) n_kv = min(n_kv, (q0 + BR - 1) / BC + 1);
+  // Blocks this wave has anything visible in (causal: keys up to its last query).
+  const int n_mine = CAUSAL ? min(n_kv, (qw0 + 31) / BC + 1) : n_kv;
+  // Leading blocks visible to every query of this wave need no mask.
+  const int n_plain = min(n_mine, CAUSAL ? qw0 / BC : N / BC);
 
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = zero16();
-  float run_max = -INFINITY;  // running max of the raw dot products q.k
-  int run_cnt = 0;            // how many visible keys attain it
-  float m2 = -INFINITY;       // current shift, in log2 units of the scaled score
-  float lsum = 0.f;           // this half's share of the row sum
-  int n_ones = 0;
+  RowState rs{-INFINITY, 0, -INFINITY, 0.f, 0};
+  f32x16 s[KB];
+  uint32_t pk[KB][8];
 
-  DirectStage<BC, D, kFwdThreads> st;
-  st.init(tid);
-  st.issue(Kg, 0, N, sK[0]);
-  st.issue(Vg, 0, N, sV[0]);
-  wait_vm0();
+  DirectStage<BC, D, kFwdThreads / 2> stg;  // group A's threads stage every tile
+  stg.init(tid & (kFwdThreads / 2 - 1));
+  if (grp == 0) {
+    stg.issue(Kg, 0, N, sK[0]);
+    wait_vm0();
+  }
   __syncthreads();
 
-  // Leading blocks visible to every query of the tile need no mask; the rest (causal diagonal,
-  // ragged tail) run through the masked body after the main loop, so the loop body has a single
-  // variant.
-  const int n_plain = min(n_kv, CAUSAL ? q0 / BC : N / BC);
-  int j = 0;
-  auto step = [&](auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const int buf = j & 1;
-    const int kv0 = j * BC;
-    if (j + 1 < n_kv) {
-      st.issue(Kg, kv0 + BC, N, sK[buf ^ 1]);
-      st.issue(Vg, kv0 + BC, N, sV[buf ^ 1]);
-    }
-    const uint16_t* tK = sK[buf];
-    const uint16_t* tV = sV[buf];
-    // S^T block kb: rows = keys kv0 + 32 kb + (8 (r/4) + 4 hh + r%4), column = this lane's query.
-    f32x16 s[KB];
+  // Matrix phase M(j): O = diag(alpha) O + V^T P^T for block j-1 (alpha and P^ from vector phase
+  // j-1), then S^T of block j.  The rescale multiplies run beside the MFMAs of other d-tiles, and
+  // the phase runs at raised wave priority so the matrix cores are fed first when both waves of a
+  // SIMD have work ready.
+  float alpha_pending = 1.f;
+  auto matrix_phase = [&](int j) {
+    __builtin_amdgcn_s_setprio(1);
+    if (j >= 1 && j - 1 < n_mine) {
+      const uint16_t* tV = sV[(j - 1) & 1];
+      const bool rescale = __any(alpha_pending != 1.f);
+      bf16x8 pb[BC / 16];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      s[kb] = zero16();
+      for (int kk = 0; kk < BC / 16; ++kk) {
+        const int kb = kk >> 1;
+        const int o4 = (kk & 1) * 4;
+        pb[kk] = make_bf16x8(pk[kb][o4], pk[kb][o4 + 1], pk[kb][o4 + 2], pk[kb][o4 + 3]);
+      }
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 kf = lds_read_row8<D>(tK, 32 * kb + l32, 16 * ks + 8 * hh);
-        s[kb] = mfma32x32x16(kf, qf[ks], s[kb]);
+      for (int dt = 0; dt < DT; ++dt) {
+        if (rescale) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha_pending;
+        }
+#pragma unroll
+        for (int kk = 0; kk < BC / 16; ++kk) {
+          const bf16x8 vf = lds_read_col8_tr<D>(tV, 16 * kk, 32 * dt, lane);
+          oacc[dt] = mfma32x32x16(vf, pb[kk], oacc[dt]);
+        }
       }
     }
-    if (MASK) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (j < n_mine) {
+      const uint16_t* tK = sK[j & 1];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        s[kb] = zero16();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 kf = lds_read_row8<D>(tK, 32 * kb + l32, 16 * ks + 8 * hh);
+          s[kb] = mfma32x32x16(kf, qf[ks], s[kb]);
+        }
+      }
+      sched_reads_ahead<KB * KS, 1, 4>();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // Vector phase V(j): online-softmax update for block j.
+  auto vector_phase = [&](int j) {
+    if (j >= n_mine) return;
+    const int kv0 = j * BC;
+    if (j >= n_plain) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -118,10 +168,10 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[kb][r]);
     tmax = halves_max(tmax);
-    const float new_max = fmaxf(run_max, tmax);
+    const float new_max = fmaxf(rs.run_max, tmax);
     // The count can only change where the block reaches the running max; skip the whole count
     // when no lane of the wave does (the common case once the max has settled).
-    if (COUNT && __any(tmax >= run_max)) {
+    if (COUNT && __any(tmax >= rs.run_max)) {
       int tcnt = 0;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -129,22 +179,21 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
         for (int r = 0; r < 16; ++r) tcnt += (s[kb][r] == tmax) ? 1 : 0;
       tcnt = halves_sum_i(tcnt);
       if (tmax == -INFINITY) tcnt = 0;
-      run_cnt = ((tmax == new_max) ? tcnt : 0) + ((run_max == new_max) ? run_cnt : 0);
+      rs.run_cnt = ((tmax == new_max) ? tcnt : 0) + ((rs.run_max == new_max) ? rs.run_cnt : 0);
     }
-    run_max = new_max;
+    rs.run_max = new_max;
     // Shift for this block (log2 units).  The sign test is unchanged by the positive factor
     // scale * log2(e), and the rule is positively homogeneous, so applying it here equals
     // applying it to the natural-log scores.
-    const float r2 = run_max * a.sl2;
+    const float r2 = rs.run_max * a.sl2;
     float m2_new = r2;
     if (MODE != 0) {
-      const bool rep = (MODE == 2) || (run_cnt > 1);
+      const bool rep = (MODE == 2) || (rs.run_cnt > 1);
       m2_new = (rep && r2 > 0.f) ? a.beta * r2 : ((rep && r2 < 0.f) ? 0.f : r2);
     }
-    const float alpha = fast_exp2(m2 - m2_new);
-    m2 = m2_new;
+    const float alpha = fast_exp2(rs.m2 - m2_new);
+    rs.m2 = m2_new;
     // P^ = exp2(S * scale * log2e - m), its row sum, and its bf16 packing for the V product.
-    uint32_t pk[KB][8];
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -155,38 +204,37 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
         psum += p0 + p1;
         const uint32_t w = pack_bf16x2(p0, p1);
         pk[kb][r >> 1] = w;
-        if (STATS) n_ones += ((w & 0xFFFFu) == kBf16One) + ((w >> 16) == kBf16One);
+        if (STATS) rs.n_ones += ((w & 0xFFFFu) == kBf16One) + ((w >> 16) == kBf16One);
       }
-    lsum = alpha * lsum + psum;
-    // Rescale O only if some lane's shift moved (alpha == 1 exactly leaves O unchanged).
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-    }
-    // O^T += V^T P^T over 16-key slabs.
-#pragma unroll
-    for (int kk = 0; kk < BC / 16; ++kk) {
-      const int kb = kk >> 1;
-      const int o4 = (kk & 1) * 4;
-      const bf16x8 pb = make_bf16x8(pk[kb][o4], pk[kb][o4 + 1], pk[kb][o4 + 2], pk[kb][o4 + 3]);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 vf = lds_read_col8_tr<D>(tV, 16 * kk, 32 * dt, lane);
-        oacc[dt] = mfma32x32x16(vf, pb, oacc[dt]);
-      }
-    }
-    wait_vm0();
-    __syncthreads();
-    ++j;
+    rs.lsum = alpha * rs.lsum + psum;
+    // O is rescaled by alpha at the start of the next matrix phase, before this block is added
+    // (alpha == 1 exactly changes nothing, so a wave where no lane's shift moved skips it).
+    alpha_pending = alpha;
   };
-  while (j < n_plain) step(std::integral_constant<bool, false>{});
-  while (j < n_kv) step(std::integral_constant<bool, true>{});
+
+  // Both groups run the same sequence M(0) V(0) M(1) V(1) ... M(n_kv), each phase closed by a
+  // workgroup barrier; group B passes one extra barrier first, so it runs one phase behind group
+  // A (A's extra barrier at the end balances the count).  Group A alone stages the tiles, at the
+  // start of its M(j): K_{j+1} (the buffer held K_{j-1}, last read by group B in phase 2j-1) and
+  // V_j (the buffer held V_{j-2}, last read by group B in phase 2j-1); it waits for them at the
+  // end of its V(j) (phase 2j+1), before K_{j+1} is read in phase 2j+2 and V_j in phase 2j+2.
+  if (grp == 1) __syncthreads();
+  for (int j = 0; j <= n_kv; ++j) {
+    if (grp == 0) {
+      if (j + 1 < n_kv) stg.issue(Kg, (j + 1) * BC, N, sK[(j + 1) & 1]);
+      if (j < n_kv) stg.issue(Vg, j * BC, N, sV[j & 1]);
+    }
+    matrix_phase(j);
+    __syncthreads();
+    vector_phase(j);
+    if (grp == 0) wait_vm0();
+    __syncthreads();
+  }
+  if (grp == 0) __syncthreads();
 
   // Epilogue: O = O^T / l, LSE = m + ln l, diagnostics.
-  const float ltot = halves_sum(lsum);
-  const int ones_tot = STATS ? halves_sum_i(n_ones) : 0;
+  const float ltot = halves_sum(rs.lsum);
+  const int ones_tot = STATS ? halves_sum_i(rs.n_ones) : 0;
   if (qrow < N) {
     const float inv = 1.f / ltot;
     uint16_t* orow = a.o + hoff + (int64_t)qrow * D;
@@ -202,9 +250,9 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
       }
     if (hh == 0) {
       const int64_t ri = (int64_t)bh * N + qrow;
-      a.lse[ri] = (m2 + __log2f(ltot)) * kLn2;
+      a.lse[ri] = (rs.m2 + __log2f(ltot)) * kLn2;
       if (STATS) {
-        if (a.dupcnt) a.dupcnt[ri] = run_cnt;
+        if (a.dupcnt) a.dupcnt[ri] = rs.run_cnt;
         if (a.ones) a.ones[ri] = ones_tot;
       }
     }
