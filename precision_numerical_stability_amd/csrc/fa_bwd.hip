@@ -156,17 +156,21 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
 
+  // Key block j lives in LDS buffer (j + p0) & 1 with p0 = n_plain & 1, so the masked blocks
+  // after the plain loop always start in buffer 0.  Every step then knows its buffer at compile
+  // time and the LDS addresses fold into instruction offsets.
+  const int p0 = n_plain & 1;
   DirectStage<BC, D, kThreads> st;
   st.init(tid);
-  st.issue(Kg, 0, N, sK[0]);
-  st.issue(Vg, 0, N, sV[0]);
+  st.issue(Kg, 0, N, sK[p0]);
+  st.issue(Vg, 0, N, sV[p0]);
   wait_vm0();
   __syncthreads();
 
   int j = 0;
-  auto step = [&](auto mask_tag) {
+  auto step = [&](auto mask_tag, auto buf_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const int buf = j & 1;
+    constexpr int buf = decltype(buf_tag)::value;
     const int kv0 = j * BC;
     if (j + 1 < n_kv) {
       st.issue(Kg, kv0 + BC, N, sK[buf ^ 1]);
@@ -197,8 +201,19 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
     __syncthreads();
     ++j;
   };
-  while (j < n_plain) step(std::integral_constant<bool, false>{});
-  while (j < n_kv) step(std::integral_constant<bool, true>{});
+  using plain = std::integral_constant<bool, false>;
+  using masked = std::integral_constant<bool, true>;
+  using buf0 = std::integral_constant<int, 0>;
+  using buf1 = std::integral_constant<int, 1>;
+  if (p0) step(plain{}, buf1{});
+  while (j < n_plain) {
+    step(plain{}, buf0{});
+    step(plain{}, buf1{});
+  }
+  while (j < n_kv) {
+    step(masked{}, buf0{});
+    if (j < n_kv) step(masked{}, buf1{});
+  }
 
   if (qrow < N) {
     uint16_t* dst = a.dq + hoff + (int64_t)qrow * D;
@@ -397,14 +412,14 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   DirectStage<BQ, D, kThreads> st;
   st.init(tid);
   float vl = 0.f, vd = 0.f;
-  auto load_rows = [&](int i) {
+  auto load_rows = [&](int i) __attribute__((always_inline)) {
     if (tid < BQ) {
       const int64_t src = roff + min(i * BQ + tid, N - 1);
       vl = a.lse[src] * kLog2e;
       vd = a.delta[src];
     }
   };
-  auto store_rows = [&](int b) {
+  auto store_rows = [&](int b) __attribute__((always_inline)) {
     if (tid < BQ) {
       sL[b][tid] = vl;
       sD[b][tid] = vd;
@@ -418,7 +433,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   static_assert(kDkvBq == kDkvBk, "the diagonal block must be the first block");
   int i = i_first;
   int buf = 0;
-  auto step = [&](auto mask_tag) {
+  auto step = [&](auto mask_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int q0 = i * BQ;
     const bool has_next = (i + 1 < n_q);

@@ -104,10 +104,13 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   // the phase runs at raised wave priority so the matrix cores are fed first when both waves of a
   // SIMD have work ready.
   float alpha_pending = 1.f;
-  auto matrix_phase = [&](int j) {
+  // PAR = j & 1 is a compile-time constant at each call site, so the LDS buffer addresses fold
+  // into instruction offsets instead of costing a vector add per read.
+  auto matrix_phase = [&](int j, auto par_tag) __attribute__((always_inline)) {
+    constexpr int PAR = decltype(par_tag)::value;
     __builtin_amdgcn_s_setprio(1);
     if (j >= 1 && j - 1 < n_mine) {
-      const uint16_t* tV = sV[(j - 1) & 1];
+      const uint16_t* tV = sV[PAR ^ 1];
       const bool rescale = __any(alpha_pending != 1.f);
       bf16x8 pb[BC / 16];
 #pragma unroll
@@ -131,7 +134,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);
     if (j < n_mine) {
-      const uint16_t* tK = sK[j & 1];
+      const uint16_t* tK = sK[PAR];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         s[kb] = zero16();
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   };
 
   // Vector phase V(j): online-softmax update for block j.
-  auto vector_phase = [&](int j) {
+  auto vector_phase = [&](int j) __attribute__((always_inline)) {
     if (j >= n_mine) return;
     const int kv0 = j * BC;
     if (j >= n_plain) {
@@ -218,18 +221,27 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   // start of its M(j): K_{j+1} (the buffer held K_{j-1}, last read by group B in phase 2j-1) and
   // V_j (the buffer held V_{j-2}, last read by group B in phase 2j-1); it waits for them at the
   // end of its V(j) (phase 2j+1), before K_{j+1} is read in phase 2j+2 and V_j in phase 2j+2.
-  if (grp == 1) __syncthreads();
-  for (int j = 0; j <= n_kv; ++j) {
+  auto iteration = [&](int j, auto par_tag) __attribute__((always_inline)) {
+    constexpr int PAR = decltype(par_tag)::value;
     if (grp == 0) {
-      if (j + 1 < n_kv) stg.issue(Kg, (j + 1) * BC, N, sK[(j + 1) & 1]);
-      if (j < n_kv) stg.issue(Vg, j * BC, N, sV[j & 1]);
+      if (j + 1 < n_kv) stg.issue(Kg, (j + 1) * BC, N, sK[PAR ^ 1]);
+      if (j < n_kv) stg.issue(Vg, j * BC, N, sV[PAR]);
     }
-    matrix_phase(j);
+    matrix_phase(j, par_tag);
     __syncthreads();
     vector_phase(j);
     if (grp == 0) wait_vm0();
     __syncthreads();
+  };
+  using even = std::integral_constant<int, 0>;
+  using odd = std::integral_constant<int, 1>;
+  if (grp == 1) __syncthreads();
+  int j = 0;
+  for (; j + 1 <= n_kv; j += 2) {
+    iteration(j, even{});
+    iteration(j + 1, odd{});
   }
+  if (j <= n_kv) iteration(j, even{});
   if (grp == 0) __syncthreads();
 
   // Epilogue: O = O^T / l, LSE = m + ln l, diagnostics.
