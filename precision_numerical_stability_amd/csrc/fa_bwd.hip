@@ -415,13 +415,13 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   auto load_rows = [&](int i) __attribute__((always_inline)) {
     if (tid < BQ) {
       const int64_t src = roff + min(i * BQ + tid, N - 1);
-      vl = a.lse[src] * kLog2e;
+      vl = a.lse[src];  // scaled when stored: no arithmetic here, so nothing waits for the load
       vd = a.delta[src];
     }
   };
   auto store_rows = [&](int b) __attribute__((always_inline)) {
     if (tid < BQ) {
-      sL[b][tid] = vl;
+      sL[b][tid] = vl * kLog2e;
       sD[b][tid] = vd;
     }
   };

@@ -134,12 +134,17 @@ __device__ __forceinline__ bf16x8 lds_read_col8_tr(const uint16_t* tile, int row
 }
 
 // Direct global -> LDS staging of a ROWS x D bf16 tile with buffer_load_dwordx4 ... lds: each
-// lane moves 16 bytes straight into LDS (lane l of a wave writes at the instruction's LDS base +
-// 16 l), so no registers hold the tile in flight.  The swizzle is applied on the global side:
-// LDS chunk position p (row p / (D/8), physical chunk p % (D/8)) is fed from logical chunk
-// physical ^ swz(row).  The buffer resource covers only rows row0 .. n_rows - 1 of the head, and
-// the hardware returns zeros for rows past it (the kernels mask those keys/queries anyway).
-// Completion is tracked by vmcnt: callers wait (wait_vm0) and then barrier before reading.
+// lane moves 16 bytes straight into LDS (lane l of a wave writes at M0 + 16 l), so no registers
+// hold the tile in flight.  The swizzle is applied on the global side: LDS chunk position p
+// (row p / (D/8), physical chunk p % (D/8)) is fed from logical chunk physical ^ swz(row).  The
+// buffer resource covers only rows row0 .. n_rows - 1 of the head, and the hardware returns zeros
+// for rows past it (the kernels mask those keys/queries anyway).
+//
+// The loads are written as inline assembly.  Issued through the compiler's LDS-DMA builtin, they
+// count as pending LDS writes, and the compiler then waits for them (vmcnt) before the next LDS
+// read of any tile: every block would stall on the next block's memory latency.  Here the
+// compiler does not see them; completion is the caller's job: wait_vm0 and then a barrier before
+// the tile is read.
 template <int ROWS, int D, int NT>
 struct DirectStage {
   static constexpr int kChunksPerRow = D / 8;
@@ -162,19 +167,28 @@ struct DirectStage {
     }
   }
   __device__ __forceinline__ void issue(const uint16_t* head, int row0, int n_rows, uint16_t* tile) const {
-    // Device pass only: with the buffer-resource builtins visible to the host pass, clang drops
-    // the host launch stubs of all but one instantiation of the kernels that call this.
 #if defined(__HIP_DEVICE_COMPILE__)
     const int rows_left = n_rows - row0;
     const int nbytes = rows_left > 0 ? rows_left * (D * 2) : 0;
-    __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(head + (int64_t)row0 * D), 0, nbytes, 0x00020000);
+    const uint64_t base = (uint64_t)(uintptr_t)(head + (int64_t)row0 * D);
+    // Buffer resource: 48-bit base, stride 0, num_records = bytes in range, raw-buffer flags.
+    i32x4 rs;
+    rs[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+    rs[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(base >> 32) & 0xFFFFu));
+    rs[2] = __builtin_amdgcn_readfirstlane(nbytes);
+    rs[3] = 0x00020000;
+    const int lds0 = (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)tile;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)((char*)tile + (wave * kPer + i) * 1024), 16,
-          voff[i], 0, 0, 0);
+      const int m0v = __builtin_amdgcn_readfirstlane(lds0 + (wave * kPer + i) * 1024);
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                   :
+                   : "v"(voff[i]), "s"(m0v), "s"(rs)
+                   : "memory", "m0");
     }
+#pragma clang diagnostic pop
 #else
     (void)head, (void)row0, (void)n_rows, (void)tile;
 #endif

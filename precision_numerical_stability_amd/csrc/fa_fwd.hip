@@ -93,10 +93,10 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
 
   DirectStage<BC, D, kFwdThreads / 2> stg;  // group A's threads stage every tile
   stg.init(tid & (kFwdThreads / 2 - 1));
-  if (grp == 0) {
-    stg.issue(Kg, 0, N, sK[0]);
-    wait_vm0();
-  }
+  if (grp == 0) stg.issue(Kg, 0, N, sK[0]);
+  // Everyone waits here: the Q fragments above are then known complete, so no wait for them is
+  // left inside the loop (where the tile loads would make it wait for those as well).
+  wait_vm0();
   __syncthreads();
 
   // Matrix phase M(j): O = diag(alpha) O + V^T P^T for block j-1 (alpha and P^ from vector phase
