@@ -248,116 +248,161 @@ struct DkvFrags {
   bf16x8 v[D / 16];
 };
 
-// S and dP for the 32 queries starting at tile row qr (one key per lane).
+// The block's MFMA stream, in time order, is 2 SB phases of L steps (L = 2 D/16 = 4 D/32):
+//   phase 0          S/dP of sub-block 0
+//   phase 2t + 1     S/dP of sub-block t + 1          (t = 0 .. SB - 2)
+//   phase 2t + 2     dV/dK of sub-block t             (t = 0 .. SB - 2)
+//   phase 2 SB - 1   dV/dK of sub-block SB - 1
+// An S/dP step is one MFMA (k-slice ks = i / 2 of S when i is even, of dP when odd) with one
+// 16-byte operand read; a dV/dK step is one MFMA (half i / (2 D/32), d-tile (i / 2) % (D/32), dV
+// when i is even, dK when odd) with one transposed operand read.  The softmax-gradient arithmetic
+// of half g of the block (sub-block g / 2, query rows 16 (g % 2) .. + 15 of it; 8 elements per lane)
+// runs element by element beside the MFMAs: halves 0 and 1 in phase 1, half g in phase g after
+// that.  Phase g reads the S/dP results of a phase that finished earlier, and the dV/dK steps of a
+// half only start after its elements are packed (half 2 SB - 1 runs in the first half of the last
+// phase, whose second half consumes it).
 template <int D>
-__device__ __forceinline__ void dkdv_sdp(const uint16_t* tQ, const uint16_t* tG, int qr, int l32, int hh,
-                                         const DkvFrags<D>& f, f32x16& s, f32x16& dp) {
-  s = zero16();
-  dp = zero16();
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    const bf16x8 qa = lds_read_row8<D>(tQ, qr + l32, 16 * ks + 8 * hh);
-    const bf16x8 ga = lds_read_row8<D>(tG, qr + l32, 16 * ks + 8 * hh);
-    s = mfma32x32x16(qa, f.k[ks], s);
-    dp = mfma32x32x16(ga, f.v[ks], dp);
+struct DkvSched {
+  static constexpr int SB = kDkvBq / 32;
+  static constexpr int L = 2 * (D / 16);
+  static_assert(L == 4 * (D / 32), "S/dP and dV/dK phases have the same length");
+  static constexpr int NSTEP = 2 * SB * L;
+  static constexpr int phase(int k) { return k / L; }
+  static constexpr bool is_sdp(int k) { return phase(k) == 0 || (phase(k) % 2 == 1 && phase(k) < 2 * SB - 1); }
+  static constexpr int sub(int k) {  // sub-block the step works on
+    const int p = phase(k);
+    if (p == 0) return 0;
+    if (p == 2 * SB - 1) return SB - 1;
+    return (p % 2 == 1) ? (p + 1) / 2 : (p - 2) / 2;
   }
-}
-
-// P = exp2(S scale log2e - LSE log2e) and dS = P (dP - delta) for 32 queries, packed to bf16 in
-// the accumulator row order.  Queries past N or (causal) before this lane's key are masked.
-template <bool MASK, bool CAUSAL, int RQ0 = 0, int RQ1 = 4>
-__device__ __forceinline__ void dkdv_grad(const float* tL, const float* tD, int qr, int q0, int N, int key,
-                                          int hh, float sl2, const f32x16& s, const f32x16& dp,
-                                          uint32_t (&pp)[8], uint32_t (&pd)[8]) {
-#pragma unroll
-  for (int rq = RQ0; rq < RQ1; ++rq) {
-    const int qi = qr + 8 * rq + 4 * hh;
-    const float4 l4 = *reinterpret_cast<const float4*>(&tL[qi]);
-    const float4 d4 = *reinterpret_cast<const float4*>(&tD[qi]);
-    const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-    const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
-    float pv[4], dsv[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = 4 * rq + u;
-      float p = fast_exp2(fmaf(s[r], sl2, -lv[u]));
-      if (MASK) {
-        const int qidx = q0 + qi + u;
-        const bool hide = (qidx >= N) || (CAUSAL && key > qidx);
-        p = hide ? 0.f : p;
-      }
-      pv[u] = p;
-      dsv[u] = p * (dp[r] - dl[u]);
-    }
-    pp[2 * rq] = pack_bf16x2(pv[0], pv[1]);
-    pp[2 * rq + 1] = pack_bf16x2(pv[2], pv[3]);
-    pd[2 * rq] = pack_bf16x2(dsv[0], dsv[1]);
-    pd[2 * rq + 1] = pack_bf16x2(dsv[2], dsv[3]);
+  // Gradient elements that run after step k's MFMA: count and the first element's flat index
+  // m = 8 g + e (g = half, e = element within it).
+  static constexpr int n_elem(int k) {
+    const int p = phase(k), j = k % L;
+    if (p == 0) return 0;
+    if (p == 1) return 16 / L;
+    if (p == 2 * SB - 1) return (j < L / 2) ? 16 / L : 0;
+    if (p % 2 == 1) return (L == 16) ? ((j % 2 == 0) ? 1 : 0) : 1;
+    return (L == 16) ? ((j % 2 == 1) ? 1 : 0) : 1;
   }
-}
-
-// dV^T += dO^T P and dK^T += Q^T dS over the two 16-query slabs of one sub-block.
-template <int D>
-__device__ __forceinline__ void dkdv_accum(const uint16_t* tQ, const uint16_t* tG, int qr, int lane,
-                                           const uint32_t (&pp)[8], const uint32_t (&pd)[8],
-                                           f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int o4 = 4 * half;
-    const bf16x8 pb = make_bf16x8(pp[o4], pp[o4 + 1], pp[o4 + 2], pp[o4 + 3]);
-    const bf16x8 sb = make_bf16x8(pd[o4], pd[o4 + 1], pd[o4 + 2], pd[o4 + 3]);
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      const bf16x8 gt = lds_read_col8_tr<D>(tG, qr + 16 * half, 32 * dt, lane);
-      const bf16x8 qt = lds_read_col8_tr<D>(tQ, qr + 16 * half, 32 * dt, lane);
-      dv[dt] = mfma32x32x16(gt, pb, dv[dt]);
-      dk[dt] = mfma32x32x16(qt, sb, dk[dt]);
-    }
+  static constexpr int first_elem(int k) {
+    const int p = phase(k), j = k % L;
+    if (p == 1) return j * (16 / L);
+    if (p == 2 * SB - 1) return 8 * p + j * (16 / L);
+    if (p % 2 == 1) return 8 * p + ((L == 16) ? j / 2 : j);
+    return 8 * p + ((L == 16) ? (j - 1) / 2 : j);
   }
-}
+  // Halves whose LSE/delta vectors are read from LDS at step k (four steps before the phase that
+  // uses them): returns a bit mask over g.
+  static constexpr int ld_halves(int k) {
+    const int p = phase(k), j = k % L;
+    if (j != L - 4 || p + 1 >= 2 * SB) return 0;
+    return (p == 0) ? 0x3 : (1 << (p + 1));
+  }
+};
 
-// Software pipeline over the sub-blocks of one block.  The softmax-gradient arithmetic of a
-// sub-block is split in two halves (accumulator rows 0-7 and 8-15 of each 16-row group, i.e. the
-// two 16-query slabs), so that every phase pairs matrix work with vector work:
-//   P1(t): S/dP of sub-block t+1 (MFMA)  with  second half of grad(t) (VALU)
-//   P2(t): dV/dK of sub-block t  (MFMA)  with  first half of grad(t+1) (VALU)
-// S/dP and the packed P/dS are double-buffered across sub-blocks.
+// One 128-query block: dV^T += dO^T P and dK^T += Q^T dS for this wave's 32 keys, with
+// S = Q K^T and dP = dO V^T recomputed per 32-query sub-block.  Operand reads run DEPTH steps
+// ahead of their MFMA through a ring of registers; every step is fenced so the order above is the
+// order the instructions issue in.
 template <int D, bool CAUSAL, bool MASK>
 __device__ __forceinline__ void dkdv_block(const uint16_t* tQ, const uint16_t* tG, const float* tL,
                                            const float* tD, int q0, int N, int key, int lane, float sl2,
                                            const DkvFrags<D>& f, f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
-  constexpr int SB = kDkvBq / 32;
-  constexpr int KSN = 2 * (D / 16);  // S/dP MFMAs per sub-block
-  constexpr int ACN = 4 * (D / 32);  // dV/dK MFMAs per sub-block
+  using S = DkvSched<D>;
+  constexpr int DT = D / 32;
+  constexpr int DEPTH = 6;
+  constexpr int RING = DEPTH + 1;  // step k's operand stays put while step k + DEPTH's is read
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   f32x16 s[2], dp[2];
   uint32_t pp[2][8], pd[2][8];
-  __builtin_amdgcn_sched_barrier(0);
-  dkdv_sdp<D>(tQ, tG, 0, l32, hh, f, s[0], dp[0]);
-  sched_reads_ahead<KSN, 1, 4>();
-  __builtin_amdgcn_sched_barrier(0);
-  dkdv_grad<MASK, CAUSAL, 0, 2>(tL, tD, 0, q0, N, key, hh, sl2, s[0], dp[0], pp[0], pd[0]);
+  bf16x8 ring[RING];
+  float4 lsl[2][2], dsl[2][2];  // [half slot][row group] LSE (log2 units) and delta vectors
+  float pt0 = 0.f, dt0 = 0.f;   // first element of the pair being packed
+
+  auto read_op = [&](auto kc) __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
+    constexpr int t = S::sub(k), i = k % S::L;
+    if constexpr (S::is_sdp(k)) {
+      constexpr int ks = i >> 1;
+      ring[k % RING] = lds_read_row8<D>((i & 1) ? tG : tQ, 32 * t + l32, 16 * ks + 8 * hh);
+    } else {
+      constexpr int half = i / (2 * DT), dt = (i >> 1) % DT;
+      ring[k % RING] = lds_read_col8_tr<D>((i & 1) ? tQ : tG, 32 * t + 16 * half, 32 * dt, lane);
+    }
+  };
+  auto read_ld = [&](auto gc) __attribute__((always_inline)) {
+    constexpr int g = decltype(gc)::value;
+    constexpr int t = g >> 1, h = g & 1;
 #pragma unroll
-  for (int t = 0; t < SB; ++t) {
-    const int c = t & 1, n = c ^ 1;
-    __builtin_amdgcn_sched_barrier(0);
-    if (t + 1 < SB) {
-      dkdv_sdp<D>(tQ, tG, 32 * (t + 1), l32, hh, f, s[n], dp[n]);
-      dkdv_grad<MASK, CAUSAL, 2, 4>(tL, tD, 32 * t, q0, N, key, hh, sl2, s[c], dp[c], pp[c], pd[c]);
-      sched_reads_ahead_valu<KSN, 1, 4, 6>();
-    } else {
-      dkdv_grad<MASK, CAUSAL, 2, 4>(tL, tD, 32 * t, q0, N, key, hh, sl2, s[c], dp[c], pp[c], pd[c]);
+    for (int w = 0; w < 2; ++w) {
+      const int qi = 32 * t + 8 * (2 * h + w) + 4 * hh;
+      lsl[g & 1][w] = *reinterpret_cast<const float4*>(&tL[qi]);
+      dsl[g & 1][w] = *reinterpret_cast<const float4*>(&tD[qi]);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    dkdv_accum<D>(tQ, tG, 32 * t, lane, pp[c], pd[c], dk, dv);
-    if (t + 1 < SB) {
-      dkdv_grad<MASK, CAUSAL, 0, 2>(tL, tD, 32 * (t + 1), q0, N, key, hh, sl2, s[n], dp[n], pp[n], pd[n]);
-      sched_reads_ahead_valu<ACN, 2, 3, 6>();
+  };
+  auto mfma_step = [&](auto kc) __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
+    constexpr int t = S::sub(k), i = k % S::L, c = t & 1;
+    const bf16x8 op = ring[k % RING];
+    if constexpr (S::is_sdp(k)) {
+      constexpr int ks = i >> 1;
+      if constexpr ((i & 1) == 0) {
+        s[c] = mfma32x32x16(op, f.k[ks], ks == 0 ? zero16() : s[c]);
+      } else {
+        dp[c] = mfma32x32x16(op, f.v[ks], ks == 0 ? zero16() : dp[c]);
+      }
     } else {
-      sched_reads_ahead<ACN, 2, 3>();
+      constexpr int half = i / (2 * DT), dt = (i >> 1) % DT, o4 = 4 * half;
+      if constexpr ((i & 1) == 0) {
+        dv[dt] = mfma32x32x16(op, make_bf16x8(pp[c][o4], pp[c][o4 + 1], pp[c][o4 + 2], pp[c][o4 + 3]), dv[dt]);
+      } else {
+        dk[dt] = mfma32x32x16(op, make_bf16x8(pd[c][o4], pd[c][o4 + 1], pd[c][o4 + 2], pd[c][o4 + 3]), dk[dt]);
+      }
     }
-  }
+  };
+  // Element e of half g: P = exp2(S scale log2e - LSE log2e), dS = P (dP - delta), masked queries
+  // (past N, or before this lane's key when causal) give zero; pairs are packed to bf16.
+  auto grad_elem = [&](auto mc) __attribute__((always_inline)) {
+    constexpr int m = decltype(mc)::value;
+    constexpr int g = m >> 3, e = m & 7;
+    constexpr int t = g >> 1, h = g & 1, c = t & 1;
+    constexpr int w = e >> 2, rq = 2 * h + w, u = e & 3, r = 4 * rq + u;
+    const float4 l4 = lsl[g & 1][w];
+    const float4 d4 = dsl[g & 1][w];
+    const float lv = u == 0 ? l4.x : u == 1 ? l4.y : u == 2 ? l4.z : l4.w;
+    const float dl = u == 0 ? d4.x : u == 1 ? d4.y : u == 2 ? d4.z : d4.w;
+    float p = fast_exp2(fmaf(s[c][r], sl2, -lv));
+    if (MASK) {
+      const int qidx = q0 + 32 * t + 8 * rq + 4 * hh + u;
+      const bool hide = (qidx >= N) || (CAUSAL && key > qidx);
+      p = hide ? 0.f : p;
+    }
+    const float ds = p * (dp[c][r] - dl);
+    if constexpr ((u & 1) == 0) {
+      pt0 = p;
+      dt0 = ds;
+    } else {
+      pp[c][2 * rq + (u >> 1)] = pack_bf16x2(pt0, p);
+      pd[c][2 * rq + (u >> 1)] = pack_bf16x2(dt0, ds);
+    }
+  };
+
+  __builtin_amdgcn_sched_barrier(0);
+  static_for<0, DEPTH>([&](auto kc) __attribute__((always_inline)) { read_op(kc); });
+  static_for<0, S::NSTEP>([&](auto kc) __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (k + DEPTH < S::NSTEP) read_op(std::integral_constant<int, k + DEPTH>{});
+    constexpr int ldm = S::ld_halves(k);
+    static_for<0, 2 * S::SB>([&](auto gc) __attribute__((always_inline)) {
+      if constexpr ((ldm >> decltype(gc)::value) & 1) read_ld(gc);
+    });
+    mfma_step(kc);
+    constexpr int m0 = S::first_elem(k), ne = S::n_elem(k);
+    static_for<m0, m0 + ne>([&](auto mc) __attribute__((always_inline)) { grad_elem(mc); });
+  });
   __builtin_amdgcn_sched_barrier(0);
 }
 

@@ -18,6 +18,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <stdint.h>
 
 namespace fa {
@@ -194,6 +196,16 @@ struct DirectStage {
 #endif
   }
 };
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E - 1, so that the body can
+// use the index in constant expressions (register-array indices, if constexpr).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // Scheduling-group masks for __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008;
