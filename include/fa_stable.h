@@ -77,7 +77,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *                   kernel's fp32 dot products;
  *   ones[b,h,i]   = number of visible keys whose unnormalised probability P^, as rounded to bf16
  *                   for the P^ V product, equals exactly 1.0.  It depends on the key-block width
- *                   returned by fa_fwd_kv_block(d), since the shift is chosen per key block from
+ *                   returned by fa_fwd_kv_block(d, causal), since the shift is chosen per key block from
  *                   the running (max, count), and key blocks are processed in ascending order. */
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
               int32_t* dupcnt, int32_t* ones,
@@ -113,9 +113,10 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
 /* Bytes of the delta workspace fa_bwd needs: B*H*N*4 (0 for invalid or empty shapes). */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 
-/* Width of the key blocks the forward processes per step for head dimension d (0 if d is not
- * supported): the granularity at which the running maximum, repeat count and shift change. */
-int fa_fwd_kv_block(int d);
+/* Width of the key blocks the forward processes per step for head dimension d and the given
+ * causal flag (0 if d is not supported): the granularity at which the running maximum, repeat
+ * count and shift change. */
+int fa_fwd_kv_block(int d, int causal);
 
 /* Static, human-readable name of a status code. */
 const char* fa_status_str(int status);

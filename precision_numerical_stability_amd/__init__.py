@@ -64,8 +64,8 @@ def fa_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
     return int(_lib.fa_bwd_workspace_bytes(B, H, N, d))
 
 
-def fa_fwd_kv_block(d: int) -> int:
-    return int(_lib.fa_fwd_kv_block(d))
+def fa_fwd_kv_block(d: int, causal: bool) -> int:
+    return int(_lib.fa_fwd_kv_block(d, int(bool(causal))))
 
 
 def _ptr(t):

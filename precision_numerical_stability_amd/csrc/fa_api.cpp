@@ -139,7 +139,7 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   return size_t(B) * size_t(H) * size_t(N) * sizeof(float);
 }
 
-int fa_fwd_kv_block(int d) { return fa::fwd_kv_block(d); }
+int fa_fwd_kv_block(int d, int causal) { return fa::fwd_kv_block(d, causal != 0); }
 
 const char* fa_status_str(int status) {
   switch (status) {

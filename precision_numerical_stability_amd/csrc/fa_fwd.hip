@@ -19,9 +19,10 @@
 //   matrix phase M(j): O += V^T P^T of block j-1, then S^T of block j     (MFMA)
 //   vector phase V(j): mask, max/count/shift, P^ of block j, rescale O    (VALU)
 // Group A runs M(0) V(0) M(1) V(1) ...; group B runs one phase behind, so in every phase one group
-// works on the matrix cores while the other works on the vector ALUs.  K and V blocks of 64 keys
-// are double-buffered in LDS: K_{j+1} and V_j are loaded during phase 2j; K_j is read in phases
-// 2j (A) and 2j+1 (B), V_j in phases 2j+2 (A) and 2j+3 (B).
+// works on the matrix cores while the other works on the vector ALUs.  K and V blocks (128 keys
+// when causal, 64 otherwise) are double-buffered in LDS: K_{j+1} and V_j are loaded during phase
+// 2j; K_j is read in phases 2j (A) and 2j+1 (B), V_j in phases 2j+2 (A) and 2j+3 (B).  Longer
+// blocks halve the barriers per key; the non-causal instances run out of registers at 128.
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -29,14 +30,17 @@
 
 namespace fa {
 
-constexpr int kFwdBc = 64;   // keys per block
+// Keys per block: 128 when causal; 64 otherwise (the non-causal instances spill at 128).
+template <bool CAUSAL>
+constexpr int fwd_bc() { return CAUSAL ? 128 : 64; }
 constexpr int kFwdBr = 256;  // queries per workgroup
 constexpr int kFwdThreads = 512;
 
 // Per-lane running state of the online softmax for one query (this lane's column).
 struct RowState {
   float run_max;  // running max of the raw dot products q.k
-  int run_cnt;    // how many visible keys attain it
+  int run_cnt;    // how many visible keys attain it (exact count: diagnostics variant)
+  float run_m2;   // second-largest raw dot product, counted with multiplicity (mode 1)
   float m2;       // current shift, in log2 units of the scaled score
   float lsum;     // this half-wave's share of the row sum
   int n_ones;     // exact-1.0 bf16 P^ values seen (stats variant)
@@ -44,8 +48,11 @@ struct RowState {
 
 template <int D, bool CAUSAL, int MODE, bool STATS>
 __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
-  constexpr int BC = kFwdBc, BR = kFwdBr, KS = D / 16, DT = D / 32, KB = BC / 32;
-  constexpr bool COUNT = (MODE == 1) || STATS;
+  constexpr int BC = fwd_bc<CAUSAL>(), BR = kFwdBr, KS = D / 16, DT = D / 32, KB = BC / 32;
+  // Mode 1 needs only whether the running maximum repeats: without the diagnostics that is
+  // decided by tracking the two largest scores; the diagnostics need the exact count.
+  constexpr bool TOP2 = (MODE == 1) && !STATS;
+  constexpr bool COUNT = STATS;
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BC * D];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][BC * D];
 
@@ -87,7 +94,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = zero16();
-  RowState rs{-INFINITY, 0, -INFINITY, 0.f, 0};
+  RowState rs{-INFINITY, 0, -INFINITY, -INFINITY, 0.f, 0};
   f32x16 s[KB];
   uint32_t pk[KB][8];
 
@@ -164,6 +171,36 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
           s[kb][r] = hide ? -INFINITY : s[kb][r];
         }
     }
+    if constexpr (TOP2) {
+      // Largest and second-largest score of the block counted with multiplicity (two chains,
+      // merged), then of both halves, then with the running pair: the maximum repeats exactly
+      // when the two are equal.  Max, min and med3 return one of their operands, so the
+      // comparison is exact.
+      float a1 = -INFINITY, a2 = -INFINITY, b1 = -INFINITY, b2 = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float x = s[kb][r], y = s[kb][r + 1];
+          if (kb & 1) {
+            b2 = fmaxf(b2, __builtin_amdgcn_fmed3f(b1, x, y));
+            b1 = fmaxf(fmaxf(b1, x), y);
+          } else {
+            a2 = fmaxf(a2, __builtin_amdgcn_fmed3f(a1, x, y));
+            a1 = fmaxf(fmaxf(a1, x), y);
+          }
+        }
+      float m1 = fmaxf(a1, b1);
+      float m2 = fmaxf(fminf(a1, b1), fmaxf(a2, b2));
+      const auto p1 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, m1), __builtin_bit_cast(int, m1), false, false);
+      const auto p2 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, m2), __builtin_bit_cast(int, m2), false, false);
+      const float u1 = __builtin_bit_cast(float, (int)p1[0]), v1 = __builtin_bit_cast(float, (int)p1[1]);
+      const float u2 = __builtin_bit_cast(float, (int)p2[0]), v2 = __builtin_bit_cast(float, (int)p2[1]);
+      m1 = fmaxf(u1, v1);
+      m2 = fmaxf(fminf(u1, v1), fmaxf(u2, v2));
+      rs.run_m2 = fmaxf(fminf(rs.run_max, m1), fmaxf(rs.run_m2, m2));
+      rs.run_max = fmaxf(rs.run_max, m1);
+    } else {
     // Block max over both halves, and (when needed) how many visible keys attain it.
     float tmax = -INFINITY;
 #pragma unroll
@@ -185,13 +222,14 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
       rs.run_cnt = ((tmax == new_max) ? tcnt : 0) + ((rs.run_max == new_max) ? rs.run_cnt : 0);
     }
     rs.run_max = new_max;
+    }
     // Shift for this block (log2 units).  The sign test is unchanged by the positive factor
     // scale * log2(e), and the rule is positively homogeneous, so applying it here equals
     // applying it to the natural-log scores.
     const float r2 = rs.run_max * a.sl2;
     float m2_new = r2;
     if (MODE != 0) {
-      const bool rep = (MODE == 2) || (rs.run_cnt > 1);
+      const bool rep = (MODE == 2) || (TOP2 ? (rs.run_m2 == rs.run_max) : (rs.run_cnt > 1));
       m2_new = (rep && r2 > 0.f) ? a.beta * r2 : ((rep && r2 < 0.f) ? 0.f : r2);
     }
     const float alpha = fast_exp2(rs.m2 - m2_new);
@@ -290,7 +328,10 @@ static hipError_t launch_fwd_mode(const FwdArgs& a, int mode, bool stats, hipStr
   return launch_fwd_t<D, CAUSAL, 2, false>(a, s);
 }
 
-int fwd_kv_block(int d) { return (d == 64 || d == 128) ? kFwdBc : 0; }
+int fwd_kv_block(int d, bool causal) {
+  if (d != 64 && d != 128) return 0;
+  return causal ? fwd_bc<true>() : fwd_bc<false>();
+}
 int fwd_q_block(int d) { return (d == 64 || d == 128) ? kFwdBr : 0; }
 
 hipError_t launch_fwd(FwdArgs a, int d, bool causal, int mode, bool stats, hipStream_t s) {

@@ -44,7 +44,7 @@ hipError_t launch_fwd(FwdArgs a, int d, bool causal, int mode, bool stats, hipSt
 hipError_t launch_bwd_delta(BwdArgs a, int d, hipStream_t s);
 hipError_t launch_bwd_dkdv(BwdArgs a, int d, bool causal, hipStream_t s);
 hipError_t launch_bwd_dq(BwdArgs a, int d, bool causal, hipStream_t s);
-int fwd_kv_block(int d);
+int fwd_kv_block(int d, bool causal);
 int fwd_q_block(int d);
 
 }  // namespace fa

@@ -47,8 +47,9 @@ def test_workspace_and_block_queries(lib):
     assert lib.fa_bwd_workspace_bytes(2, 3, 5, 64) == 2 * 3 * 5 * 4
     assert lib.fa_bwd_workspace_bytes(-1, 3, 5, 64) == 0
     assert lib.fa_bwd_workspace_bytes(1, 1, 8, 96) == 0
-    assert lib.fa_fwd_kv_block(64) > 0 and lib.fa_fwd_kv_block(128) > 0
-    assert lib.fa_fwd_kv_block(80) == 0
+    for causal in (0, 1):
+        assert lib.fa_fwd_kv_block(64, causal) > 0 and lib.fa_fwd_kv_block(128, causal) > 0
+        assert lib.fa_fwd_kv_block(80, causal) == 0
 
 
 P = ctypes.c_void_p(0x7F0000000000)  # 16-byte aligned, never dereferenced

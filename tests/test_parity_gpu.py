@@ -118,7 +118,7 @@ def test_config1_tiny_duplicates(fa, mode):
     t = make_inputs(cfg)
     res = run_fa(fa, t, cfg.causal, cfg.scale, mode)
     fr = check_head(res, t, 0, 0, cfg.causal, cfg.scale, mode, counts_exact=True, ones_exact=True,
-                    bc=fa.fa_fwd_kv_block(cfg.d))
+                    bc=fa.fa_fwd_kv_block(cfg.d, cfg.causal))
     assert np.all(res["dup"][0, 0, :8] == 2)
     if mode != 0:
         # rows 0..7 have a repeated positive maximum: no exact 1.0 once shifted
@@ -171,7 +171,7 @@ def test_config5_long_tie_grid(fa, mode):
     _say("config5", mode)
     t = make_inputs(cfg)
     res = run_fa(fa, t, cfg.causal, cfg.scale, mode, bwd=(mode == 1))
-    bc = fa.fa_fwd_kv_block(cfg.d)
+    bc = fa.fa_fwd_kv_block(cfg.d, cfg.causal)
     for h in (0, 31):
         fr = check_head(res, t, 0, h, cfg.causal, cfg.scale, mode, grads=(mode == 1 and h == 0),
                         counts_exact=True, ones_exact=True, bc=bc)
@@ -212,7 +212,31 @@ def test_grid_ties_small(fa, causal):
         res = run_fa(fa, t, causal, scale, mode)
         for h in range(2):
             check_head(res, t, 0, h, causal, scale, mode, counts_exact=True, ones_exact=True,
-                       bc=fa.fa_fwd_kv_block(128))
+                       bc=fa.fa_fwd_kv_block(128, causal))
+
+
+@pytest.mark.parametrize("case", ["config1", "grid-causal", "grid-full", "config5"])
+def test_mode1_repeat_test_matches_counting_variant(fa, case):
+    """Without diagnostics, mode 1 decides "the running maximum repeats" from the two largest
+    scores instead of the exact count; every decision must agree with the counting variant, so
+    O and LSE must be bit-identical to it on tie-heavy inputs."""
+    _say("mode1-fast", case)
+    if case == "config1":
+        cfg = CONFIGS[1]
+        t, causal, scale = make_inputs(cfg), cfg.causal, cfg.scale
+    elif case == "config5":
+        cfg = CONFIGS[5]
+        t, causal, scale = make_inputs(cfg, H=4), cfg.causal, cfg.scale
+    else:
+        t = grid_inputs(2, 2, 453, 128, seed=91)
+        causal, scale = case == "grid-causal", 128 ** -0.5
+    g = _to_dev(t)
+    o1, l1, dup, _ = fa.forward(g["q"], g["k"], g["v"], causal, scale, BETA, 1, stats=True)
+    o2, l2 = fa.forward(g["q"], g["k"], g["v"], causal, scale, BETA, 1)
+    torch.cuda.synchronize()
+    assert (dup > 1).any(), "the case has no repeated maxima"
+    assert torch.equal(o1, o2), f"O differs in {(o1 != o2).sum().item()} elements"
+    assert torch.equal(l1, l2), f"LSE differs in {(l1 != l2).sum().item()} rows"
 
 
 def test_deterministic_and_stream_ordered(fa):
