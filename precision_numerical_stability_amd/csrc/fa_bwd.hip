@@ -162,8 +162,10 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
   const int p0 = n_plain & 1;
   DirectStage<BC, D, kThreads> st;
   st.init(tid);
-  st.issue(Kg, 0, N, sK[p0]);
-  st.issue(Vg, 0, N, sV[p0]);
+  constexpr uint32_t kTileBytes = BC * D * 2;
+  const uint32_t aK = lds_addr(&sK[0][0]), aV = lds_addr(&sV[0][0]);
+  st.issue(Kg, 0, N, aK + p0 * kTileBytes);
+  st.issue(Vg, 0, N, aV + p0 * kTileBytes);
   wait_vm0();
   __syncthreads();
 
@@ -173,8 +175,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
     constexpr int buf = decltype(buf_tag)::value;
     const int kv0 = j * BC;
     if (j + 1 < n_kv) {
-      st.issue(Kg, kv0 + BC, N, sK[buf ^ 1]);
-      st.issue(Vg, kv0 + BC, N, sV[buf ^ 1]);
+      st.issue(Kg, kv0 + BC, N, aK + (buf ^ 1) * kTileBytes);
+      st.issue(Vg, kv0 + BC, N, aV + (buf ^ 1) * kTileBytes);
     }
     const uint16_t* tK = sK[buf];
     const uint16_t* tV = sV[buf];
@@ -456,6 +458,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
 
   DirectStage<BQ, D, kThreads> st;
   st.init(tid);
+  constexpr uint32_t kTileBytes = BQ * D * 2;
+  const uint32_t aQ = lds_addr(&sQ[0][0]), aG = lds_addr(&sG[0][0]);
   float vl = 0.f, vd = 0.f;
   auto load_rows = [&](int i) __attribute__((always_inline)) {
     if (tid < BQ) {
@@ -483,8 +487,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
     const int q0 = i * BQ;
     const bool has_next = (i + 1 < n_q);
     if (has_next) {
-      st.issue(Qg, q0 + BQ, N, sQ[buf ^ 1]);
-      st.issue(Gg, q0 + BQ, N, sG[buf ^ 1]);
+      st.issue(Qg, q0 + BQ, N, aQ + (buf ^ 1) * kTileBytes);
+      st.issue(Gg, q0 + BQ, N, aG + (buf ^ 1) * kTileBytes);
       load_rows(i + 1);
     }
     dkdv_block<D, CAUSAL, MASK>(sQ[buf], sG[buf], sL[buf], sD[buf], q0, N, key, lane, a.sl2, f, dk, dv);
@@ -498,8 +502,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   using plain = std::integral_constant<bool, false>;
 
   if (i < n_q) {
-    st.issue(Qg, i * BQ, N, sQ[0]);
-    st.issue(Gg, i * BQ, N, sG[0]);
+    st.issue(Qg, i * BQ, N, aQ);
+    st.issue(Gg, i * BQ, N, aG);
     load_rows(i);
     store_rows(0);
   }

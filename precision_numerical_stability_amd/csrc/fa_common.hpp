@@ -135,6 +135,13 @@ __device__ __forceinline__ bf16x8 lds_read_col8_tr(const uint16_t* tile, int row
   return make_bf16x8((uint32_t)a[0], (uint32_t)a[1], (uint32_t)b[0], (uint32_t)b[1]);
 }
 
+// Byte address in LDS of a __shared__ object.  Take it from the array itself (not from a pointer
+// that may have passed through a select): the cast then folds to the object's LDS offset.
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(T* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) T*)p;
+}
+
 // Direct global -> LDS staging of a ROWS x D bf16 tile with buffer_load_dwordx4 ... lds: each
 // lane moves 16 bytes straight into LDS (lane l of a wave writes at M0 + 16 l), so no registers
 // hold the tile in flight.  The swizzle is applied on the global side: LDS chunk position p
@@ -168,7 +175,8 @@ struct DirectStage {
       voff[i] = r * (D * 2) + ((pc ^ swz<D>(r)) << 4);
     }
   }
-  __device__ __forceinline__ void issue(const uint16_t* head, int row0, int n_rows, uint16_t* tile) const {
+  // lds: byte address of the destination tile in LDS (lds_addr of the __shared__ array).
+  __device__ __forceinline__ void issue(const uint16_t* head, int row0, int n_rows, uint32_t lds) const {
 #if defined(__HIP_DEVICE_COMPILE__)
     const int rows_left = n_rows - row0;
     const int nbytes = rows_left > 0 ? rows_left * (D * 2) : 0;
@@ -179,7 +187,7 @@ struct DirectStage {
     rs[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(base >> 32) & 0xFFFFu));
     rs[2] = __builtin_amdgcn_readfirstlane(nbytes);
     rs[3] = 0x00020000;
-    const int lds0 = (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)tile;
+    const int lds0 = (int)lds;
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 #pragma unroll
@@ -192,7 +200,7 @@ struct DirectStage {
     }
 #pragma clang diagnostic pop
 #else
-    (void)head, (void)row0, (void)n_rows, (void)tile;
+    (void)head, (void)row0, (void)n_rows, (void)lds;
 #endif
   }
 };

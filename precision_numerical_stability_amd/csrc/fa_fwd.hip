@@ -100,7 +100,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
 
   DirectStage<BC, D, kFwdThreads / 2> stg;  // group A's threads stage every tile
   stg.init(tid & (kFwdThreads / 2 - 1));
-  if (grp == 0) stg.issue(Kg, 0, N, sK[0]);
+  constexpr uint32_t kTileBytes = BC * D * 2;
+  const uint32_t aK = lds_addr(&sK[0][0]), aV = lds_addr(&sV[0][0]);
+  if (grp == 0) stg.issue(Kg, 0, N, aK);
   // Everyone waits here: the Q fragments above are then known complete, so no wait for them is
   // left inside the loop (where the tile loads would make it wait for those as well).
   wait_vm0();
@@ -255,18 +257,17 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
 
   // Both groups run the same sequence M(0) V(0) M(1) V(1) ... M(n_kv), each phase closed by a
   // workgroup barrier; group B passes one extra barrier first, so it runs one phase behind group
-  // A (A's extra barrier at the end balances the count).  Group A alone stages the tiles, at the
-  // start of its M(j): K_{j+1} (the buffer held K_{j-1}, last read by group B in phase 2j-1) and
-  // V_j (the buffer held V_{j-2}, last read by group B in phase 2j-1); it waits for them at the
-  // end of its V(j) (phase 2j+1), before K_{j+1} is read in phase 2j+2 and V_j in phase 2j+2.
+  // A (A's extra barrier at the end balances the count).  Group A alone stages the tiles: K_{j+1}
+  // at the start of its M(j) (phase 2j; the buffer held K_{j-1}, last read by group B in phase
+  // 2j-1) and V_j at the start of its V(j) (phase 2j+1; the buffer held V_{j-2}, last read in
+  // phase 2j-1).  Splitting them keeps either phase from carrying all the load issue.  A waits
+  // for both at the end of its V(j), before K_{j+1} and V_j are read in phase 2j+2.
   auto iteration = [&](int j, auto par_tag) __attribute__((always_inline)) {
     constexpr int PAR = decltype(par_tag)::value;
-    if (grp == 0) {
-      if (j + 1 < n_kv) stg.issue(Kg, (j + 1) * BC, N, sK[PAR ^ 1]);
-      if (j < n_kv) stg.issue(Vg, j * BC, N, sV[PAR]);
-    }
+    if (grp == 0 && j + 1 < n_kv) stg.issue(Kg, (j + 1) * BC, N, aK + (PAR ^ 1) * kTileBytes);
     matrix_phase(j, par_tag);
     __syncthreads();
+    if (grp == 0 && j < n_kv) stg.issue(Vg, j * BC, N, aV + PAR * kTileBytes);
     vector_phase(j);
     if (grp == 0) wait_vm0();
     __syncthreads();
