@@ -108,54 +108,77 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   wait_vm0();
   __syncthreads();
 
-  // Matrix phase M(j): O = diag(alpha) O + V^T P^T for block j-1 (alpha and P^ from vector phase
-  // j-1), then S^T of block j.  The rescale multiplies run beside the MFMAs of other d-tiles, and
-  // the phase runs at raised wave priority so the matrix cores are fed first when both waves of a
-  // SIMD have work ready.
   float alpha_pending = 1.f;
-  // PAR = j & 1 is a compile-time constant at each call site, so the LDS buffer addresses fold
-  // into instruction offsets instead of costing a vector add per read.
+  // The matrix phase is one straight-line stream of MFMA steps, each fenced: steps [0, NPV) add
+  // V^T P^T of the previous block (d-tile by d-tile), steps [NPV, NPV + NSS) compute S^T of this
+  // block.  The LDS operand of step k + MDEPTH is read at step k into a register ring; the
+  // rescale of O by the previous block's alpha runs beside the MFMAs (d-tile 0 before the first
+  // step, d-tile t + 1 during the steps of d-tile t; alpha == 1 leaves O unchanged).
+  constexpr int KK = BC / 16;
+  constexpr int NPV = DT * KK, NSS = KB * KS;
+  constexpr int MDEPTH = 4, MRING = MDEPTH + 1;
+  bf16x8 mring[MRING];
+  auto m_read = [&](auto kc, const uint16_t* tV, const uint16_t* tK) __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
+    if constexpr (k < NPV) {
+      constexpr int dt = k / KK, kk = k % KK;
+      mring[k % MRING] = lds_read_col8_tr<D>(tV, 16 * kk, 32 * dt, lane);
+    } else {
+      constexpr int i = k - NPV, kb = i / KS, ks = i % KS;
+      mring[k % MRING] = lds_read_row8<D>(tK, 32 * kb + l32, 16 * ks + 8 * hh);
+    }
+  };
+  auto m_step = [&](auto kc) __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
+    const bf16x8 op = mring[k % MRING];
+    if constexpr (k < NPV) {
+      constexpr int dt = k / KK, kk = k % KK, o4 = (kk & 1) * 4;
+      oacc[dt] = mfma32x32x16(op, make_bf16x8(pk[kk >> 1][o4], pk[kk >> 1][o4 + 1], pk[kk >> 1][o4 + 2],
+                                              pk[kk >> 1][o4 + 3]), oacc[dt]);
+      if constexpr (dt + 1 < DT) {
+        constexpr int per = 16 / KK;
+#pragma unroll
+        for (int r = per * kk; r < per * (kk + 1); ++r) oacc[dt + 1][r] *= alpha_pending;
+      }
+    } else {
+      constexpr int i = k - NPV, kb = i / KS, ks = i % KS;
+      s[kb] = mfma32x32x16(op, qf[ks], ks == 0 ? zero16() : s[kb]);
+    }
+  };
+  auto m_stream = [&](auto k0c, auto k1c, const uint16_t* tV, const uint16_t* tK) __attribute__((always_inline)) {
+    constexpr int K0 = decltype(k0c)::value, K1 = decltype(k1c)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<K0, (K0 + MDEPTH < K1 ? K0 + MDEPTH : K1)>(
+        [&](auto kc) __attribute__((always_inline)) { m_read(kc, tV, tK); });
+    if constexpr (K0 == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[0][r] *= alpha_pending;
+    }
+    static_for<K0, K1>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (k + MDEPTH < K1) m_read(std::integral_constant<int, k + MDEPTH>{}, tV, tK);
+      m_step(kc);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using c0 = std::integral_constant<int, 0>;
+  using cpv = std::integral_constant<int, NPV>;
+  using cend = std::integral_constant<int, NPV + NSS>;
+
+  // Matrix phase M(j): O = diag(alpha) O + V^T P^T for block j-1 (alpha and P^ from vector phase
+  // j-1), then S^T of block j, at raised wave priority so the matrix cores are fed first when
+  // both waves of a SIMD have work ready.  PAR = j & 1 is a compile-time constant at each call
+  // site, so the LDS buffer addresses fold into instruction offsets.
   auto matrix_phase = [&](int j, auto par_tag) __attribute__((always_inline)) {
     constexpr int PAR = decltype(par_tag)::value;
+    const uint16_t* tV = sV[PAR ^ 1];
+    const uint16_t* tK = sK[PAR];
+    const bool pv = j >= 1 && j - 1 < n_mine;
+    const bool sc = j < n_mine;
     __builtin_amdgcn_s_setprio(1);
-    if (j >= 1 && j - 1 < n_mine) {
-      const uint16_t* tV = sV[PAR ^ 1];
-      const bool rescale = __any(alpha_pending != 1.f);
-      bf16x8 pb[BC / 16];
-#pragma unroll
-      for (int kk = 0; kk < BC / 16; ++kk) {
-        const int kb = kk >> 1;
-        const int o4 = (kk & 1) * 4;
-        pb[kk] = make_bf16x8(pk[kb][o4], pk[kb][o4 + 1], pk[kb][o4 + 2], pk[kb][o4 + 3]);
-      }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        if (rescale) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha_pending;
-        }
-#pragma unroll
-        for (int kk = 0; kk < BC / 16; ++kk) {
-          const bf16x8 vf = lds_read_col8_tr<D>(tV, 16 * kk, 32 * dt, lane);
-          oacc[dt] = mfma32x32x16(vf, pb[kk], oacc[dt]);
-        }
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (j < n_mine) {
-      const uint16_t* tK = sK[PAR];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        s[kb] = zero16();
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 kf = lds_read_row8<D>(tK, 32 * kb + l32, 16 * ks + 8 * hh);
-          s[kb] = mfma32x32x16(kf, qf[ks], s[kb]);
-        }
-      }
-      sched_reads_ahead<KB * KS, 1, 4>();
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    if (pv) m_stream(c0{}, cpv{}, tV, tK);
+    if (sc) m_stream(cpv{}, cend{}, tV, tK);
     __builtin_amdgcn_s_setprio(0);
   };
 
