@@ -177,6 +177,24 @@ def main():
     ms_delta = time_events(run_stage(fa.FA_BWD_DELTA), it, stream)
     ms_dkdv = time_events(run_stage(fa.FA_BWD_DKDV), it, stream)
     ms_dq = time_events(run_stage(fa.FA_BWD_DQ), it, stream)
+    # The forward in the other tie modes (the headline runs stable_flag = mode).
+    ms_fwd_mode = {}
+    for m in (0, 1, 2):
+        ms_fwd_mode[str(m)] = time_events(
+            lambda m=m: fa.fa_fwd(q, k, v, o, lse, causal, scale, 1.25, m, stream=stream), it, stream)
+    run_fwd()  # leave this mode's output in o for the checks below
+    # Measured ceilings on this GPU: a pure-MFMA kernel and a device-to-device copy.
+    n_wg, iters = 2048, 512
+    probe_out = torch.empty(n_wg * 256, dtype=torch.float32, device=dev)
+    fa.fa_probe_mfma_peak(probe_out, n_wg, iters, stream=stream)
+    ms_probe = time_events(lambda: fa.fa_probe_mfma_peak(probe_out, n_wg, iters, stream=stream), 3, stream)
+    mfma_peak_meas = n_wg * 4 * iters * 32 * 32768 / (ms_probe * 1e-3) / 1e12
+    csrc_t = torch.empty(256 << 20, dtype=torch.float32, device=dev)
+    cdst_t = torch.empty_like(csrc_t)
+    cdst_t.copy_(csrc_t)
+    ms_copy = time_events(lambda: cdst_t.copy_(csrc_t), 5, stream)
+    copy_gbs = 2 * csrc_t.numel() * 4 / (ms_copy * 1e-3) / 1e9
+    del csrc_t, cdst_t, probe_out
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all() and torch.isfinite(dq.float()).all()
     if args.calib_copy_mib > 0:
@@ -217,10 +235,15 @@ def main():
     for name, (bnd, work_k, ms_k) in alg.items():
         if bnd == "mfma":
             tf = work_k / (ms_k * 1e-3) / 1e12
-            kernels[name] = {"ms": ms_k, "TFLOP/s": tf, "frac_bf16_peak": tf / PEAK_BF16_TFLOPS}
+            kernels[name] = {"ms": ms_k, "TFLOP/s": tf, "frac_bf16_peak": tf / PEAK_BF16_TFLOPS,
+                             "frac_measured_mfma": tf / mfma_peak_meas}
         else:
             gbs = work_k / (ms_k * 1e-3) / 1e9
-            kernels[name] = {"ms": ms_k, "GB/s": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS}
+            kernels[name] = {"ms": ms_k, "GB/s": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS,
+                             "frac_measured_copy": gbs / copy_gbs}
+    fwd_modes = {m: {"ms": t_, "TFLOP/s": ff / (t_ * 1e-3) / 1e12,
+                     "frac_bf16_peak": ff / (t_ * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+                 for m, t_ in ms_fwd_mode.items()}
 
     out = {
         "metric": METRIC,
@@ -242,6 +265,9 @@ def main():
         "fwd_frac_peak": fwd_tf / PEAK_BF16_TFLOPS,
         "fwdbwd_tflops": value,
         "fwdbwd_frac_peak": value / PEAK_BF16_TFLOPS,
+        "fwd_by_stable_flag": fwd_modes,
+        "measured_ceilings": {"mfma_bf16_TFLOP/s": mfma_peak_meas, "d2d_copy_GB/s": copy_gbs},
+        "fwdbwd_frac_measured_mfma": value / mfma_peak_meas,
         "exact_causal_pairs": pairs,
         "kernels": kernels,
         "roofline": roof,

@@ -118,6 +118,14 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  * count and shift change. */
 int fa_fwd_kv_block(int d, int causal);
 
+/* Measurement helper, not part of the attention path: runs n_workgroups workgroups of 256
+ * threads, each wave issuing iters * 32 dense bf16 32x32x16 MFMAs (2^15 flop each) on register
+ * operands, and writes one float per thread to out (caller-owned device memory of
+ * n_workgroups * 256 floats, 4-byte aligned; the values are meaningless).  Timing it gives the
+ * MFMA rate the GPU sustains, reported beside the published peak.  Errors: FA_ERR_NULL,
+ * FA_ERR_PARAM (n_workgroups outside 1 .. 2^20 or iters < 1), FA_ERR_ALIGN, FA_ERR_HIP. */
+int fa_probe_mfma_peak(float* out, int n_workgroups, int iters, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* fa_status_str(int status);
 

@@ -33,7 +33,7 @@ TIE_ANTICIPATE = 2
 DEFAULT_BETA = 1.25
 
 __all__ = [
-    "fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_bytes", "fa_fwd_kv_block", "fa_status_str",
+    "fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_bytes", "fa_fwd_kv_block", "fa_probe_mfma_peak", "fa_status_str",
     "fa_last_hip_error", "FaError", "forward", "backward", "attention", "STANDARD", "TIE_RULE",
     "TIE_ANTICIPATE", "DEFAULT_BETA", "library_path",
 ]
@@ -66,6 +66,18 @@ def fa_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
 
 def fa_fwd_kv_block(d: int, causal: bool) -> int:
     return int(_lib.fa_fwd_kv_block(d, int(bool(causal))))
+
+
+def fa_probe_mfma_peak(out, n_workgroups: int, iters: int, stream=None) -> None:
+    """Measurement helper (not part of the attention path): n_workgroups x 256 threads of pure
+    bf16 MFMA work, iters * 32 MFMAs of 2^15 flop per wave; out is a float32 CUDA tensor of at
+    least n_workgroups * 256 elements."""
+    if out.dtype != torch.float32 or not out.is_cuda or out.numel() < n_workgroups * 256:
+        raise ValueError("out must be a float32 CUDA tensor of n_workgroups * 256 elements")
+    st = _stream_handle(out.device, stream)
+    rc = _lib.fa_probe_mfma_peak(_ptr(out), int(n_workgroups), int(iters), st)
+    if rc != FA_OK:
+        raise FaError(rc)
 
 
 def _ptr(t):

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "_lib")
 LIBNAME = "libfa_stable.so"
-SOURCES = ("fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip")
+SOURCES = ("fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_probe.hip")
 ARCH = "gfx950"
 
 # -packed-fp32-ops keeps the compiler from forming packed fp32 VALU instructions.

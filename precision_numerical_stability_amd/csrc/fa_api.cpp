@@ -141,6 +141,13 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
 
 int fa_fwd_kv_block(int d, int causal) { return fa::fwd_kv_block(d, causal != 0); }
 
+int fa_probe_mfma_peak(float* out, int n_workgroups, int iters, void* stream) {
+  if (!out) return FA_ERR_NULL;
+  if (n_workgroups < 1 || iters < 1 || n_workgroups > (1 << 20)) return FA_ERR_PARAM;
+  if (!aligned(out, 4)) return FA_ERR_ALIGN;
+  return hip_status(fa::launch_mfma_peak(out, n_workgroups, iters, static_cast<hipStream_t>(stream)));
+}
+
 const char* fa_status_str(int status) {
   switch (status) {
     case FA_OK: return "FA_OK";

@@ -45,6 +45,7 @@ hipError_t launch_bwd_delta(BwdArgs a, int d, hipStream_t s);
 hipError_t launch_bwd_dkdv(BwdArgs a, int d, bool causal, hipStream_t s);
 hipError_t launch_bwd_dq(BwdArgs a, int d, bool causal, hipStream_t s);
 int fwd_kv_block(int d, bool causal);
+hipError_t launch_mfma_peak(float* out, int n_workgroups, int iters, hipStream_t stream);
 int fwd_q_block(int d);
 
 }  // namespace fa

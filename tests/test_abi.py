@@ -138,3 +138,11 @@ def test_single_hip_runtime_mapped():
     import precision_numerical_stability_amd  # noqa: F401
     from precision_numerical_stability_amd import _ffi
     assert len(_ffi.hip_runtimes_mapped()) <= 1
+
+
+def test_probe_rejects_bad_arguments(lib):
+    assert lib.fa_probe_mfma_peak(None, 4, 4, None) == 1  # FA_ERR_NULL
+    assert lib.fa_probe_mfma_peak(P, 0, 4, None) == 4  # FA_ERR_PARAM
+    assert lib.fa_probe_mfma_peak(P, 4, 0, None) == 4
+    assert lib.fa_probe_mfma_peak(P, (1 << 20) + 1, 4, None) == 4
+    assert lib.fa_probe_mfma_peak(ctypes.c_void_p(0x7F0000000002), 4, 4, None) == 5  # FA_ERR_ALIGN
