@@ -4,14 +4,16 @@ TEST INFRASTRUCTURE: imported only by the test suite, the package smoke check an
 CPU-baseline leg of the benchmark.  It shares no code with the HIP library and never imports it.
 """
 from .attention import (MODE_STANDARD, MODE_TIE_RULE, MODE_TIE_ANTICIPATE, bf16_round, visible,
-                        scaled_scores, row_max_and_repeats, stable_shift, forward, backward,
+                        scaled_scores, row_max_and_repeats, stable_shift, forward, forward_rows,
+                        backward, dq_rows,
                         probabilities, forward_bhnd, backward_bhnd, flops_forward,
                         exact_causal_pairs, ForwardResult, BackwardResult)
 from .tiled import tiled_forward, tiled_ones
 
 __all__ = [
     "MODE_STANDARD", "MODE_TIE_RULE", "MODE_TIE_ANTICIPATE", "bf16_round", "visible",
-    "scaled_scores", "row_max_and_repeats", "stable_shift", "forward", "backward",
+    "scaled_scores", "row_max_and_repeats", "stable_shift", "forward", "forward_rows",
+    "backward", "dq_rows",
     "probabilities", "forward_bhnd", "backward_bhnd", "flops_forward", "exact_causal_pairs",
     "ForwardResult", "BackwardResult", "tiled_forward", "tiled_ones",
 ]

@@ -108,13 +108,30 @@ class ForwardResult:
     ones: np.ndarray  # [N] count of bf16(exp(S - m)) == 1.0 over visible keys (int64)
 
 
-def forward(q, k, v, causal, scale, beta=1.25, mode=MODE_STANDARD, row_chunk=1024):
-    """One head of attention: q [N, d], k [N, d], v [N, d] (float64).
+def forward_rows(q, k, v, rows, causal, scale, beta=1.25, mode=MODE_STANDARD):
+    """The forward of one head for the query rows `rows` (absolute indices into q; the causal mask
+    uses them), evaluated without tiling: P_hat = exp(S - m), l = rowsum(P_hat),
+    O = diag(l)^-1 P_hat V and LSE = m + ln l ([BF16-FA] §2.1, [FA-practice] §3.3,
+    [FA-backward] §2).  Returns a ForwardResult whose arrays are indexed like `rows`."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    rows = np.asarray(rows)
+    mask = visible(rows, k.shape[0], causal)
+    s = scaled_scores(q[rows], k, scale, mask)
+    rm, rs = row_max_and_repeats(s)
+    m = stable_shift(rm, rs, beta, mode)
+    p_hat = np.exp(s - m[:, None])  # exp(-inf) = 0 on invisible keys
+    l = p_hat.sum(axis=1)
+    o = (p_hat @ v) / l[:, None]
+    lse = m + np.log(l)
+    ones = np.sum((bf16_round(p_hat) == 1.0) & mask, axis=1)
+    return ForwardResult(o, lse, rm, rs, m, l, ones)
 
-    Following the forward of [BF16-FA] §2.1 evaluated without tiling: P_hat = exp(S - m),
-    l = rowsum(P_hat), O = diag(l)^-1 P_hat V, and the logsumexp LSE = m + ln l that the backward
-    uses to rebuild P ([FA-practice] §3.3, [FA-backward] §2).
-    """
+
+def forward(q, k, v, causal, scale, beta=1.25, mode=MODE_STANDARD, row_chunk=1024):
+    """One head of attention: q [N, d], k [N, d], v [N, d] (float64): forward_rows over all rows,
+    in chunks of row_chunk rows to bound memory."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -128,16 +145,9 @@ def forward(q, k, v, causal, scale, beta=1.25, mode=MODE_STANDARD, row_chunk=102
     ones = np.zeros(n, dtype=np.int64)
     for r0 in range(0, n, row_chunk):
         rows = np.arange(r0, min(n, r0 + row_chunk))
-        mask = visible(rows, k.shape[0], causal)
-        s = scaled_scores(q[rows], k, scale, mask)
-        rm, rs = row_max_and_repeats(s)
-        m = stable_shift(rm, rs, beta, mode)
-        p_hat = np.exp(s - m[:, None])  # exp(-inf) = 0 on invisible keys
-        l = p_hat.sum(axis=1)
-        o[rows] = (p_hat @ v) / l[:, None]
-        lse[rows] = m + np.log(l)
-        rm_all[rows], rs_all[rows], m_all[rows], l_all[rows] = rm, rs, m, l
-        ones[rows] = np.sum((bf16_round(p_hat) == 1.0) & mask, axis=1)
+        fr = forward_rows(q, k, v, rows, causal, scale, beta, mode)
+        o[rows], lse[rows] = fr.o, fr.lse
+        rm_all[rows], rs_all[rows], m_all[rows], l_all[rows], ones[rows] = fr.rm, fr.rs, fr.m, fr.l, fr.ones
     return ForwardResult(o, lse, rm_all, rs_all, m_all, l_all, ones)
 
 
@@ -178,14 +188,36 @@ def backward(q, k, v, do, causal, scale, o=None, lse=None, row_chunk=1024):
     delta = np.sum(do * o, axis=1)
     for r0 in range(0, n, row_chunk):
         rows = np.arange(r0, min(n, r0 + row_chunk))
-        mask = visible(rows, k.shape[0], causal)
-        p = probabilities(q[rows], k, scale, lse[rows], mask)
+        p, ds = _grad_rows(q, k, v, do, rows, causal, scale, lse[rows], delta[rows])
         dv += p.T @ do[rows]
-        dp = do[rows] @ v.T
-        ds = p * (dp - delta[rows][:, None])
         dq[rows] = scale * (ds @ k)
         dk += scale * (ds.T @ q[rows])
     return BackwardResult(dq, dk, dv, delta)
+
+
+def _grad_rows(q, k, v, do, rows, causal, scale, lse_rows, delta_rows):
+    """P and dS = P o (dP - delta), dP = dO V^T, for the query rows `rows` ([FA-backward] §2,
+    [BF16-FA] §3.1)."""
+    mask = visible(rows, k.shape[0], causal)
+    p = probabilities(q[rows], k, scale, lse_rows, mask)
+    dp = do[rows] @ v.T
+    ds = p * (dp - delta_rows[:, None])
+    return p, ds
+
+
+def dq_rows(q, k, v, do, rows, causal, scale, beta=1.25, mode=MODE_STANDARD):
+    """dQ and delta of one head for the query rows `rows` alone: each needs only its own row's
+    O and LSE (forward_rows) and all keys, so it can be evaluated at any sequence length.
+    Returns (dq [len(rows), d], delta [len(rows)])."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    rows = np.asarray(rows)
+    fr = forward_rows(q, k, v, rows, causal, scale, beta, mode)
+    delta = np.sum(do[rows] * fr.o, axis=1)
+    _, ds = _grad_rows(q, k, v, do, rows, causal, scale, fr.lse, delta)
+    return scale * (ds @ k), delta
 
 
 def _heads(x):

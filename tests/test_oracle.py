@@ -467,3 +467,23 @@ def test_planted_count_merge_mistake_is_caught():
         r = np.maximum(r, tm)
     assert np.array_equal(good, oracle.forward(t["q"], t["k"], t["v"], False, 0.3, BETA, 1).rs)
     assert not np.array_equal(c, good)
+
+
+def test_row_subset_functions_match_full_oracle():
+    """forward_rows and dq_rows (used to check sampled rows at sequence lengths the full oracle
+    cannot afford) evaluate the same definitions as forward/backward on any subset of rows, in
+    any order, with the causal mask taken from the absolute row index."""
+    rng = np.random.default_rng(5)
+    n, d = 70, 16
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    rows = np.array([69, 0, 33, 1, 64, 17])
+    for causal in (False, True):
+        for mode in (0, 1, 2):
+            full = oracle.forward(q, k, v, causal, 0.3, 1.25, mode, row_chunk=16)
+            part = oracle.forward_rows(q, k, v, rows, causal, 0.3, 1.25, mode)
+            for name in ("o", "lse", "rm", "rs", "m", "l", "ones"):
+                assert np.array_equal(getattr(part, name), getattr(full, name)[rows]), name
+        br = oracle.backward(q, k, v, do, causal, 0.3, row_chunk=16)
+        dq, delta = oracle.dq_rows(q, k, v, do, rows, causal, 0.3)
+        np.testing.assert_allclose(dq, br.dq[rows], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(delta, br.delta[rows], rtol=1e-12, atol=1e-12)

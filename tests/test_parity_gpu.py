@@ -239,6 +239,43 @@ def test_mode1_repeat_test_matches_counting_variant(fa, case):
     assert torch.equal(l1, l2), f"LSE differs in {(l1 != l2).sum().item()} rows"
 
 
+@pytest.mark.parametrize("causal,N", [(True, 1 << 20), (False, 1 << 18)])
+def test_long_sequence_sampled_rows_and_invariants(fa, causal, N):
+    """One head at a sequence length far beyond the other cases (2^20 keys causal, 2^18 not;
+    the kernels' limit is N d 2 < 2^31 bytes per head): sampled rows of O, LSE and dQ against the
+    oracle evaluated row by row, and dK, dV through identities that hold at any size:
+    sum_j dK_j = 0, sum_j dV_j = sum_i dO_i, <Q, dQ> = <K, dK>."""
+    d = 128
+    scale = d ** -0.5
+    _say("long", causal, N)
+    t = randn_inputs(1, 1, N, d, seed=4242 + int(causal))
+    g = _to_dev(t)
+    o, lse = fa.forward(g["q"], g["k"], g["v"], causal, scale, BETA, 1)
+    dq, dk, dv = fa.backward(g["q"], g["k"], g["v"], o, lse, g["do"], causal, scale)
+    torch.cuda.synchronize()
+    for x in (o, lse, dq, dk, dv):
+        assert torch.isfinite(x.float()).all()
+    rng = np.random.default_rng(N)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 255, 256, 4095, 4096, N // 2, N - 2, N - 1],
+                                     rng.integers(0, N, 5)]))
+    x = {k_: v_[0, 0].to(torch.float64).numpy() for k_, v_ in t.items()}
+    fr = oracle.forward_rows(x["q"], x["k"], x["v"], rows, causal, scale, BETA, 1)
+    check_o(o[0, 0, rows].float().cpu().numpy(), fr.o, "O rows")
+    check_lse(lse[0, 0, rows].cpu().numpy(), fr.lse)
+    dq_ref, _ = oracle.dq_rows(x["q"], x["k"], x["v"], x["do"], rows, causal, scale)
+    check_grad(dq[0, 0, rows].float().cpu().numpy(), dq_ref, "dQ rows")
+    del x, t
+    q64, k64 = g["q"][0, 0].double(), g["k"][0, 0].double()
+    dq64, dk64, dv64, do64 = dq[0, 0].double(), dk[0, 0].double(), dv[0, 0].double(), g["do"][0, 0].double()
+    mass_k = dk64.abs().sum(0).max().item()
+    assert dk64.sum(0).abs().max().item() <= 2e-3 * mass_k, "sum of dK rows is not zero"
+    mass_v = dv64.abs().sum(0).max().item()
+    assert (dv64.sum(0) - do64.sum(0)).abs().max().item() <= 2e-3 * mass_v, "sum dV != sum dO"
+    a_ = (q64 * dq64).sum().item()
+    b_ = (k64 * dk64).sum().item()
+    assert abs(a_ - b_) <= 1e-2 * (q64 * dq64).abs().sum().item(), f"<Q,dQ> {a_} != <K,dK> {b_}"
+
+
 def test_deterministic_and_stream_ordered(fa):
     _say("determinism")
     t = make_inputs(2, B=2)
