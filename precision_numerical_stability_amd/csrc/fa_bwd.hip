@@ -12,6 +12,8 @@
 // workgroup, so results are deterministic.  All three run on the caller's stream in order.
 #include <type_traits>
 
+#include <climits>
+
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -87,9 +89,11 @@ __device__ __forceinline__ void dq_grad(const f32x16& s, const f32x16& dp, int k
       const int rr = r + u;
       float p = fast_exp2(fmaf(s[rr], sl2, -lse2));
       if (MASK) {
-        const int key = key0 + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-        const bool hide = (key >= N) || (CAUSAL && key > qrow);
-        p = hide ? 0.f : p;
+        // Key key0 + c + 4 hh, c = 8 (rr / 4) + rr % 4, is hidden past N or (causal) past the
+        // lane's query: c > lim.
+        const int lim = min(CAUSAL ? qrow - key0 - 4 * hh : INT_MAX, N - 1 - key0 - 4 * hh);
+        const int c = 8 * (rr >> 2) + (rr & 3);
+        p = (c > lim) ? 0.f : p;
       }
       ds2[u] = p * (dp[rr] - dlt);
     }
@@ -377,9 +381,12 @@ __device__ __forceinline__ void dkdv_block(const uint16_t* tQ, const uint16_t* t
     const float dl = u == 0 ? d4.x : u == 1 ? d4.y : u == 2 ? d4.z : d4.w;
     float p = fast_exp2(fmaf(s[c][r], sl2, -lv));
     if (MASK) {
-      const int qidx = q0 + 32 * t + 8 * rq + 4 * hh + u;
-      const bool hide = (qidx >= N) || (CAUSAL && key > qidx);
-      p = hide ? 0.f : p;
+      // Query q0 + c + 4 hh, c = 32 t + 8 rq + u, is hidden past N or (causal) before this
+      // lane's key: c > hi or c < lo.
+      const int hi = N - 1 - q0 - 4 * hh;
+      const int lo = CAUSAL ? key - q0 - 4 * hh : INT_MIN;
+      constexpr int c = 32 * t + 8 * rq + u;
+      p = (c > hi || c < lo) ? 0.f : p;
     }
     const float ds = p * (dp[c][r] - dl);
     if constexpr ((u & 1) == 0) {
