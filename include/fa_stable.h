@@ -84,6 +84,24 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int N, int d, int causal, float scale, float beta, int stable_flag,
               void* stream);
 
+/* Forward pass with training monitors and a numerics option (every diagnostic pointer may be
+ * NULL; when any is non-NULL the diagnostics variant of the kernel runs):
+ *   dupcnt, ones  as for fa_fwd_ex;
+ *   smin[b,h,i]   = min over visible keys j of the scaled score S_ij = scale q_i.k_j, and
+ *   smax[b,h,i]   = max over visible keys of S_ij: the range of the softmax input that
+ *                   "Flash Attention低精度训练稳定性优化实践" (jsqmd.com/news/761560) §5 says to
+ *                   monitor besides NaNs, fp32 [B,H,N].
+ * flags: 0, or FA_FWD_COMPENSATED_SUM: the row sum l of the unnormalised probabilities is kept
+ *   with a compensated (Kahan) running sum across key blocks, which the ijyty.com article §7.2
+ *   recommends for the softmax denominator of large models; O and lse then use that sum.
+ *   Other bits -> FA_ERR_PARAM.
+ * fa_fwd_ex(...) == fa_fwd_stats(..., dupcnt, ones, NULL, NULL, ..., 0, stream). */
+#define FA_FWD_COMPENSATED_SUM 1
+int fa_fwd_stats(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int32_t* dupcnt, int32_t* ones, float* smin, float* smax,
+                 int B, int H, int N, int d, int causal, float scale, float beta, int stable_flag,
+                 int flags, void* stream);
+
 /* Backward pass: from q, k, v, the forward's o and lse, and the upstream gradient dO, writes
  * dq, dk, dv [B,H,N,d] bf16.  delta_ws is a caller-owned fp32 workspace of
  * fa_bwd_workspace_bytes(B,H,N,d) bytes; on return (in stream order) it holds

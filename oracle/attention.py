@@ -106,6 +106,7 @@ class ForwardResult:
     m: np.ndarray  # [N] the row shift actually used
     l: np.ndarray  # [N] sum of the unnormalised probabilities exp(S - m)
     ones: np.ndarray  # [N] count of bf16(exp(S - m)) == 1.0 over visible keys (int64)
+    smin: np.ndarray  # [N] row min of the scaled scores over visible keys
 
 
 def forward_rows(q, k, v, rows, causal, scale, beta=1.25, mode=MODE_STANDARD):
@@ -126,7 +127,9 @@ def forward_rows(q, k, v, rows, causal, scale, beta=1.25, mode=MODE_STANDARD):
     o = (p_hat @ v) / l[:, None]
     lse = m + np.log(l)
     ones = np.sum((bf16_round(p_hat) == 1.0) & mask, axis=1)
-    return ForwardResult(o, lse, rm, rs, m, l, ones)
+    # The range of the softmax input, to be monitored ([FA-practice] §5): min over visible keys.
+    smin = np.min(np.where(mask, s, np.inf), axis=1)
+    return ForwardResult(o, lse, rm, rs, m, l, ones, smin)
 
 
 def forward(q, k, v, causal, scale, beta=1.25, mode=MODE_STANDARD, row_chunk=1024):
@@ -143,12 +146,14 @@ def forward(q, k, v, causal, scale, beta=1.25, mode=MODE_STANDARD, row_chunk=102
     m_all = np.zeros(n)
     l_all = np.zeros(n)
     ones = np.zeros(n, dtype=np.int64)
+    smin = np.zeros(n)
     for r0 in range(0, n, row_chunk):
         rows = np.arange(r0, min(n, r0 + row_chunk))
         fr = forward_rows(q, k, v, rows, causal, scale, beta, mode)
         o[rows], lse[rows] = fr.o, fr.lse
         rm_all[rows], rs_all[rows], m_all[rows], l_all[rows], ones[rows] = fr.rm, fr.rs, fr.m, fr.l, fr.ones
-    return ForwardResult(o, lse, rm_all, rs_all, m_all, l_all, ones)
+        smin[rows] = fr.smin
+    return ForwardResult(o, lse, rm_all, rs_all, m_all, l_all, ones, smin)
 
 
 def probabilities(q_rows, k, scale, lse_rows, mask):
@@ -240,6 +245,7 @@ def forward_bhnd(q, k, v, causal, scale, beta=1.25, mode=MODE_STANDARD, heads=No
         "m": np.zeros((B, H, N)),
         "l": np.zeros((B, H, N)),
         "ones": np.zeros((B, H, N), dtype=np.int64),
+        "smin": np.zeros((B, H, N)),
     }
     pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
     for b, h in pairs:

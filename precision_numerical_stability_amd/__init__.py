@@ -19,7 +19,8 @@ import torch  # loaded first so that its HIP runtime is the one this library bin
 
 from . import _ffi
 from ._ffi import (FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_PARAM, FA_ERR_ALIGN,
-                   FA_ERR_HIP, FA_BWD_DELTA, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL)
+                   FA_ERR_HIP, FA_BWD_DELTA, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL,
+                   FA_FWD_COMPENSATED_SUM)
 
 _lib = _ffi.load_library()
 
@@ -33,7 +34,7 @@ TIE_ANTICIPATE = 2
 DEFAULT_BETA = 1.25
 
 __all__ = [
-    "fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_bytes", "fa_fwd_kv_block", "fa_probe_mfma_peak", "fa_status_str",
+    "fa_fwd", "fa_fwd_ex", "fa_fwd_stats", "FA_FWD_COMPENSATED_SUM", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_bytes", "fa_fwd_kv_block", "fa_probe_mfma_peak", "fa_status_str",
     "fa_last_hip_error", "FaError", "forward", "backward", "attention", "STANDARD", "TIE_RULE",
     "TIE_ANTICIPATE", "DEFAULT_BETA", "library_path",
 ]
@@ -123,6 +124,26 @@ def fa_fwd_ex(q, k, v, o, lse, dupcnt, ones, causal, scale, beta, stable_flag, s
     _raise(st)
 
 
+def fa_fwd_stats(q, k, v, o, lse, dupcnt, ones, smin, smax, causal, scale, beta, stable_flag,
+                 flags=0, stream=None):
+    """Call fa_fwd_stats on torch tensors: as fa_fwd_ex, plus smin and smax [B,H,N] fp32 or None
+    (per-row min and max of the scaled visible scores) and flags (FA_FWD_COMPENSATED_SUM)."""
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check(t, name, torch.bfloat16, (B, H, N, d))
+    _check(lse, "lse", torch.float32, (B, H, N))
+    for name, t in (("dupcnt", dupcnt), ("ones", ones)):
+        if t is not None:
+            _check(t, name, torch.int32, (B, H, N))
+    for name, t in (("smin", smin), ("smax", smax)):
+        if t is not None:
+            _check(t, name, torch.float32, (B, H, N))
+    st = _lib.fa_fwd_stats(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dupcnt), _ptr(ones),
+                           _ptr(smin), _ptr(smax), B, H, N, d, int(causal), float(scale), float(beta),
+                           int(stable_flag), int(flags), _stream_handle(q.device, stream))
+    _raise(st)
+
+
 def fa_fwd(q, k, v, o, lse, causal, scale, beta, stable_flag, stream=None):
     fa_fwd_ex(q, k, v, o, lse, None, None, causal, scale, beta, stable_flag, stream)
 
@@ -163,19 +184,28 @@ def _default_scale(d):
 
 
 def forward(q, k, v, causal=False, scale=None, beta=DEFAULT_BETA, stable_flag=TIE_RULE,
-            stats=False, stream=None):
-    """Allocate outputs and run the forward.  Returns (o, lse) or, with stats=True,
-    (o, lse, dupcnt, ones)."""
+            stats=False, monitor=False, compensated_sum=False, stream=None):
+    """Allocate outputs and run the forward.  Returns (o, lse), plus (dupcnt, ones) with
+    stats=True, plus (smin, smax) with monitor=True.  compensated_sum selects the Kahan row sum."""
     B, H, N, d = q.shape
     scale = _default_scale(d) if scale is None else scale
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    dup = ones = None
+    dup = ones = smin = smax = None
     if stats:
         dup = torch.empty((B, H, N), dtype=torch.int32, device=q.device)
         ones = torch.empty((B, H, N), dtype=torch.int32, device=q.device)
-    fa_fwd_ex(q, k, v, o, lse, dup, ones, causal, scale, beta, stable_flag, stream)
-    return (o, lse, dup, ones) if stats else (o, lse)
+    if monitor:
+        smin = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        smax = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    flags = FA_FWD_COMPENSATED_SUM if compensated_sum else 0
+    fa_fwd_stats(q, k, v, o, lse, dup, ones, smin, smax, causal, scale, beta, stable_flag, flags, stream)
+    out = (o, lse)
+    if stats:
+        out += (dup, ones)
+    if monitor:
+        out += (smin, smax)
+    return out
 
 
 def backward(q, k, v, o, lse, dO, causal=False, scale=None, stream=None):

@@ -51,16 +51,18 @@ int hip_status(hipError_t e) {
 
 extern "C" {
 
-int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* dupcnt,
-              int32_t* ones, int B, int H, int N, int d, int causal, float scale, float beta,
-              int stable_flag, void* stream) {
+int fa_fwd_stats(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* dupcnt,
+                 int32_t* ones, float* smin, float* smax, int B, int H, int N, int d, int causal,
+                 float scale, float beta, int stable_flag, int flags, void* stream) {
   bool empty = false;
   const int st = check_common(B, H, N, d, causal, scale, beta, stable_flag, &empty);
   if (st != FA_OK) return st;
+  if ((flags & ~FA_FWD_COMPENSATED_SUM) != 0) return FA_ERR_PARAM;
   if (empty) return FA_OK;
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return FA_ERR_ALIGN;
   if (!aligned(lse, 4) || (dupcnt && !aligned(dupcnt, 4)) || (ones && !aligned(ones, 4))) return FA_ERR_ALIGN;
+  if ((smin && !aligned(smin, 4)) || (smax && !aligned(smax, 4))) return FA_ERR_ALIGN;
 
   fa::FwdArgs a{};
   a.q = static_cast<const uint16_t*>(q);
@@ -70,12 +72,24 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
   a.lse = lse;
   a.dupcnt = dupcnt;
   a.ones = ones;
+  a.smin = smin;
+  a.smax = smax;
   a.BH = B * H;
   a.N = N;
   a.sl2 = scale * 1.4426950408889634f;
+  a.scale = scale;
   a.beta = beta;
-  const bool stats = (dupcnt != nullptr) || (ones != nullptr);
-  return hip_status(fa::launch_fwd(a, d, causal != 0, stable_flag, stats, static_cast<hipStream_t>(stream)));
+  const bool stats = dupcnt || ones || smin || smax;
+  const bool kahan = (flags & FA_FWD_COMPENSATED_SUM) != 0;
+  return hip_status(
+      fa::launch_fwd(a, d, causal != 0, stable_flag, stats, kahan, static_cast<hipStream_t>(stream)));
+}
+
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* dupcnt,
+              int32_t* ones, int B, int H, int N, int d, int causal, float scale, float beta,
+              int stable_flag, void* stream) {
+  return fa_fwd_stats(q, k, v, o, lse, dupcnt, ones, nullptr, nullptr, B, H, N, d, causal, scale, beta,
+                      stable_flag, 0, stream);
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,

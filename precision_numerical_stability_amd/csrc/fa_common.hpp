@@ -71,6 +71,11 @@ __device__ __forceinline__ float halves_max(float x) {
   auto s = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
   return fmaxf(__builtin_bit_cast(float, (int)s[0]), __builtin_bit_cast(float, (int)s[1]));
 }
+__device__ __forceinline__ float halves_min(float x) {
+  int xi = __builtin_bit_cast(int, x);
+  auto s = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return fminf(__builtin_bit_cast(float, (int)s[0]), __builtin_bit_cast(float, (int)s[1]));
+}
 __device__ __forceinline__ float halves_sum(float x) {
   int xi = __builtin_bit_cast(int, x);
   auto s = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);

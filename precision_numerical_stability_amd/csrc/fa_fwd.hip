@@ -43,10 +43,12 @@ struct RowState {
   float run_m2;   // second-largest raw dot product, counted with multiplicity (mode 1)
   float m2;       // current shift, in log2 units of the scaled score
   float lsum;     // this half-wave's share of the row sum
+  float lcomp;    // its compensation term (compensated-sum variant): lost low-order part, negated
+  float run_min;  // running min of the raw dot products over visible keys (diagnostics variant)
   int n_ones;     // exact-1.0 bf16 P^ values seen (stats variant)
 };
 
-template <int D, bool CAUSAL, int MODE, bool STATS>
+template <int D, bool CAUSAL, int MODE, bool STATS, bool KAHAN>
 __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   constexpr int BC = fwd_bc<CAUSAL>(), BR = kFwdBr, KS = D / 16, DT = D / 32, KB = BC / 32;
   // Mode 1 needs only whether the running maximum repeats: without the diagnostics that is
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = zero16();
-  RowState rs{-INFINITY, 0, -INFINITY, -INFINITY, 0.f, 0};
+  RowState rs{-INFINITY, 0, -INFINITY, -INFINITY, 0.f, 0.f, INFINITY, 0};
   f32x16 s[KB];
   uint32_t pk[KB][8];
 
@@ -196,6 +198,14 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
           s[kb][r] = hide ? -INFINITY : s[kb][r];
         }
     }
+    if (STATS) {
+      // Min over visible keys: hidden entries are exactly -inf, visible scores are finite.
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          rs.run_min = fminf(rs.run_min, s[kb][r] == -INFINITY ? INFINITY : s[kb][r]);
+    }
     if constexpr (TOP2) {
       // Largest and second-largest score of the block counted with multiplicity (two chains,
       // merged), then of both halves, then with the running pair: the maximum repeats exactly
@@ -272,7 +282,17 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
         pk[kb][r >> 1] = w;
         if (STATS) rs.n_ones += ((w & 0xFFFFu) == kBf16One) + ((w >> 16) == kBf16One);
       }
-    rs.lsum = alpha * rs.lsum + psum;
+    if constexpr (KAHAN) {
+      // Compensated running sum: the previous sum and its compensation scale by alpha together;
+      // the low-order part lost in adding this block's sum is kept (negated) in lcomp.
+      const float lprev = alpha * rs.lsum;
+      const float y = psum - alpha * rs.lcomp;
+      const float t = lprev + y;
+      rs.lcomp = (t - lprev) - y;
+      rs.lsum = t;
+    } else {
+      rs.lsum = alpha * rs.lsum + psum;
+    }
     // O is rescaled by alpha at the start of the next matrix phase, before this block is added
     // (alpha == 1 exactly changes nothing, so a wave where no lane's shift moved skips it).
     alpha_pending = alpha;
@@ -307,7 +327,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   if (grp == 0) __syncthreads();
 
   // Epilogue: O = O^T / l, LSE = m + ln l, diagnostics.
-  const float ltot = halves_sum(rs.lsum);
+  const float ltot = KAHAN ? halves_sum(rs.lsum - rs.lcomp) : halves_sum(rs.lsum);
+  const float row_min = STATS ? halves_min(rs.run_min) : 0.f;
   const int ones_tot = STATS ? halves_sum_i(rs.n_ones) : 0;
   if (qrow < N) {
     const float inv = 1.f / ltot;
@@ -328,28 +349,31 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
       if (STATS) {
         if (a.dupcnt) a.dupcnt[ri] = rs.run_cnt;
         if (a.ones) a.ones[ri] = ones_tot;
+        if (a.smin) a.smin[ri] = row_min * a.scale;
+        if (a.smax) a.smax[ri] = rs.run_max * a.scale;
       }
     }
   }
 }
 
-template <int D, bool CAUSAL, int MODE, bool STATS>
+template <int D, bool CAUSAL, int MODE, bool STATS, bool KAHAN>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const int grid = a.n_tiles * a.BH;
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, MODE, STATS>), dim3(grid), dim3(kFwdThreads), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, MODE, STATS, KAHAN>), dim3(grid), dim3(kFwdThreads), 0, stream, a);
   return hipGetLastError();
 }
 
+template <int D, bool CAUSAL, bool STATS, bool KAHAN>
+static hipError_t launch_fwd_m(const FwdArgs& a, int mode, hipStream_t s) {
+  if (mode == 0) return launch_fwd_t<D, CAUSAL, 0, STATS, KAHAN>(a, s);
+  if (mode == 1) return launch_fwd_t<D, CAUSAL, 1, STATS, KAHAN>(a, s);
+  return launch_fwd_t<D, CAUSAL, 2, STATS, KAHAN>(a, s);
+}
+
 template <int D, bool CAUSAL>
-static hipError_t launch_fwd_mode(const FwdArgs& a, int mode, bool stats, hipStream_t s) {
-  if (stats) {
-    if (mode == 0) return launch_fwd_t<D, CAUSAL, 0, true>(a, s);
-    if (mode == 1) return launch_fwd_t<D, CAUSAL, 1, true>(a, s);
-    return launch_fwd_t<D, CAUSAL, 2, true>(a, s);
-  }
-  if (mode == 0) return launch_fwd_t<D, CAUSAL, 0, false>(a, s);
-  if (mode == 1) return launch_fwd_t<D, CAUSAL, 1, false>(a, s);
-  return launch_fwd_t<D, CAUSAL, 2, false>(a, s);
+static hipError_t launch_fwd_mode(const FwdArgs& a, int mode, bool stats, bool kahan, hipStream_t s) {
+  if (stats) return kahan ? launch_fwd_m<D, CAUSAL, true, true>(a, mode, s) : launch_fwd_m<D, CAUSAL, true, false>(a, mode, s);
+  return kahan ? launch_fwd_m<D, CAUSAL, false, true>(a, mode, s) : launch_fwd_m<D, CAUSAL, false, false>(a, mode, s);
 }
 
 int fwd_kv_block(int d, bool causal) {
@@ -358,10 +382,13 @@ int fwd_kv_block(int d, bool causal) {
 }
 int fwd_q_block(int d) { return (d == 64 || d == 128) ? kFwdBr : 0; }
 
-hipError_t launch_fwd(FwdArgs a, int d, bool causal, int mode, bool stats, hipStream_t s) {
+hipError_t launch_fwd(FwdArgs a, int d, bool causal, int mode, bool stats, bool kahan, hipStream_t s) {
   a.n_tiles = (a.N + kFwdBr - 1) / kFwdBr;
-  if (d == 64) return causal ? launch_fwd_mode<64, true>(a, mode, stats, s) : launch_fwd_mode<64, false>(a, mode, stats, s);
-  return causal ? launch_fwd_mode<128, true>(a, mode, stats, s) : launch_fwd_mode<128, false>(a, mode, stats, s);
+  if (d == 64)
+    return causal ? launch_fwd_mode<64, true>(a, mode, stats, kahan, s)
+                  : launch_fwd_mode<64, false>(a, mode, stats, kahan, s);
+  return causal ? launch_fwd_mode<128, true>(a, mode, stats, kahan, s)
+                : launch_fwd_mode<128, false>(a, mode, stats, kahan, s);
 }
 
 }  // namespace fa

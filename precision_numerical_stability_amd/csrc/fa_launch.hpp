@@ -15,10 +15,13 @@ struct FwdArgs {
   float* lse;
   int32_t* dupcnt;  // may be null
   int32_t* ones;    // may be null
+  float* smin;      // may be null: per-row min of the scaled visible scores
+  float* smax;      // may be null: per-row max of the scaled visible scores
   int BH;           // B * H
   int N;
   int n_tiles;      // query tiles per head (set by launch_fwd)
   float sl2;        // scale * log2(e)
+  float scale;
   float beta;
 };
 
@@ -40,7 +43,7 @@ struct BwdArgs {
   float sl2;    // scale * log2(e)
 };
 
-hipError_t launch_fwd(FwdArgs a, int d, bool causal, int mode, bool stats, hipStream_t s);
+hipError_t launch_fwd(FwdArgs a, int d, bool causal, int mode, bool stats, bool kahan, hipStream_t s);
 hipError_t launch_bwd_delta(BwdArgs a, int d, hipStream_t s);
 hipError_t launch_bwd_dkdv(BwdArgs a, int d, bool causal, hipStream_t s);
 hipError_t launch_bwd_dq(BwdArgs a, int d, bool causal, hipStream_t s);

@@ -146,3 +146,14 @@ def test_probe_rejects_bad_arguments(lib):
     assert lib.fa_probe_mfma_peak(P, 4, 0, None) == 4
     assert lib.fa_probe_mfma_peak(P, (1 << 20) + 1, 4, None) == 4
     assert lib.fa_probe_mfma_peak(ctypes.c_void_p(0x7F0000000002), 4, 4, None) == 5  # FA_ERR_ALIGN
+
+
+def test_fwd_stats_rejects_bad_arguments(lib):
+    def call(smin=P, smax=P, flags=0, q=P):
+        return lib.fa_fwd_stats(q, P, P, P, P, None, None, smin, smax, 1, 2, 128, 64, 0, 0.125, 1.25,
+                                1, flags, None)
+    assert call(flags=2) == 4  # FA_ERR_PARAM: unknown flag bit
+    assert call(flags=-1) == 4
+    assert call(q=None) == 1  # FA_ERR_NULL
+    assert call(smin=ctypes.c_void_p(0x7F0000000002)) == 5  # FA_ERR_ALIGN
+    assert call(smax=ctypes.c_void_p(0x7F0000000001)) == 5

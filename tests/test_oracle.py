@@ -114,6 +114,11 @@ def test_brute_force_tiny(causal, mode):
         fr = oracle.forward(q, k, v, causal, 0.7, BETA, mode)
         np.testing.assert_allclose(fr.o, o_ref, rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(fr.lse, lse_ref, rtol=1e-12, atol=1e-12)
+        # row range of the scaled scores, by scalar loops over the visible keys
+        for i in range(n):
+            vis = [0.7 * sum(a * b for a, b in zip(q[i], k[j])) for j in range(n) if not causal or j <= i]
+            assert math.isclose(fr.rm[i], max(vis), rel_tol=1e-12, abs_tol=1e-12)
+            assert math.isclose(fr.smin[i], min(vis), rel_tol=1e-12, abs_tol=1e-12)
 
 
 # ----------------------------------------------------------------------------------------------
@@ -481,7 +486,7 @@ def test_row_subset_functions_match_full_oracle():
         for mode in (0, 1, 2):
             full = oracle.forward(q, k, v, causal, 0.3, 1.25, mode, row_chunk=16)
             part = oracle.forward_rows(q, k, v, rows, causal, 0.3, 1.25, mode)
-            for name in ("o", "lse", "rm", "rs", "m", "l", "ones"):
+            for name in ("o", "lse", "rm", "rs", "m", "l", "ones", "smin"):
                 assert np.array_equal(getattr(part, name), getattr(full, name)[rows]), name
         br = oracle.backward(q, k, v, do, causal, 0.3, row_chunk=16)
         dq, delta = oracle.dq_rows(q, k, v, do, rows, causal, 0.3)

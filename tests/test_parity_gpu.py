@@ -276,6 +276,74 @@ def test_long_sequence_sampled_rows_and_invariants(fa, causal, N):
     assert abs(a_ - b_) <= 1e-2 * (q64 * dq64).abs().sum().item(), f"<Q,dQ> {a_} != <K,dK> {b_}"
 
 
+@pytest.mark.parametrize("case", ["config2", "config3", "ragged-causal", "ragged-full", "grid"])
+def test_monitor_score_range(fa, case):
+    """Per-row min and max of the scaled visible scores (the monitored softmax input range)
+    against the oracle; O and LSE of the monitoring call equal the plain call's bit for bit."""
+    _say("monitor", case)
+    if case in ("config2", "config3"):
+        cfg = CONFIGS[2 if case == "config2" else 3]
+        t, causal, scale, heads = make_inputs(cfg, B=2), cfg.causal, cfg.scale, [(0, 0), (1, 3)]
+    elif case == "grid":
+        t, causal, scale, heads = grid_inputs(1, 2, 300, 128, seed=23), True, 128 ** -0.5, [(0, 0), (0, 1)]
+    else:
+        causal = case == "ragged-causal"
+        t, scale, heads = randn_inputs(1, 2, 333, 64, seed=31), 0.125, [(0, 0), (0, 1)]
+    g = _to_dev(t)
+    o, lse, smin, smax = fa.forward(g["q"], g["k"], g["v"], causal, scale, BETA, 1, monitor=True)
+    o2, lse2 = fa.forward(g["q"], g["k"], g["v"], causal, scale, BETA, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    for b, h in heads:
+        x = _np64(t, b, h)
+        fr = oracle.forward(x["q"], x["k"], x["v"], causal, scale, BETA, 1)
+        for got, ref, name in ((smin, fr.smin, "smin"), (smax, fr.rm, "smax")):
+            err = np.abs(got[b, h].cpu().numpy() - ref)
+            assert np.all(err <= 1e-5 * (1 + np.abs(ref))), f"{name}[{b},{h}] max error {err.max():.3e}"
+
+
+@pytest.mark.parametrize("cid", [2, 4])
+def test_compensated_sum_parity(fa, cid):
+    """The compensated-sum forward meets the same bounds; its LSE drives the same backward."""
+    cfg = CONFIGS[cid]
+    _say("compensated", cid)
+    t = make_inputs(cfg, H=2) if cid == 4 else make_inputs(cfg, B=1)
+    g = _to_dev(t)
+    o, lse = fa.forward(g["q"], g["k"], g["v"], cfg.causal, cfg.scale, BETA, 1, compensated_sum=True)
+    dq, dk, dv = fa.backward(g["q"], g["k"], g["v"], o, lse, g["do"], cfg.causal, cfg.scale)
+    torch.cuda.synchronize()
+    res = {"o": o.float().cpu().numpy(), "lse": lse.cpu().numpy(), "dq": dq.float().cpu().numpy(),
+           "dk": dk.float().cpu().numpy(), "dv": dv.float().cpu().numpy()}
+    check_head(res, t, 0, 1, cfg.causal, cfg.scale, 1)
+
+
+def test_compensated_sum_keeps_small_terms():
+    """One exact maximum (S = 0) and 65535 keys at S = -25 exactly: each key block adds ~4e-10
+    to a running sum near 1, below half an fp32 ulp of 1, so a plain running sum drops the lanes'
+    share next to the maximum; the compensated sum keeps it.  LSE = log(1 + 65535 e^-25)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import precision_numerical_stability_amd as fa
+    N, d, scale = 65536, 64, 0.125
+    _say("compensated-small-terms")
+    q = torch.zeros(1, 1, N, d)
+    q[..., 0] = 1.0
+    k = torch.zeros(1, 1, N, d)
+    k[0, 0, 1:, 0] = -200.0  # scale * q.k = -25 exactly for every key but key 0
+    v = torch.randn(1, 1, N, d, generator=torch.Generator().manual_seed(8))
+    g = {n_: x_.to(torch.bfloat16).to(DEV) for n_, x_ in (("q", q), ("k", k), ("v", v))}
+    _, lse_plain = fa.forward(g["q"], g["k"], g["v"], False, scale, BETA, 0)
+    _, lse_comp = fa.forward(g["q"], g["k"], g["v"], False, scale, BETA, 0, compensated_sum=True)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, N // 3, N - 1])
+    x = {n_: g[n_][0, 0].double().cpu().numpy() for n_ in ("q", "k", "v")}
+    ref = oracle.forward_rows(x["q"], x["k"], x["v"], rows, False, scale, BETA, 0).lse
+    err_plain = np.abs(lse_plain[0, 0, rows].cpu().numpy() - ref)
+    err_comp = np.abs(lse_comp[0, 0, rows].cpu().numpy() - ref)
+    assert np.all(err_comp <= 1.5e-7), err_comp
+    assert np.all(err_plain >= 3e-7), err_plain
+
+
 def test_deterministic_and_stream_ordered(fa):
     _say("determinism")
     t = make_inputs(2, B=2)
