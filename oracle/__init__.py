@@ -7,7 +7,8 @@ from .attention import (MODE_STANDARD, MODE_TIE_RULE, MODE_TIE_ANTICIPATE, bf16_
                         scaled_scores, row_max_and_repeats, stable_shift, forward, forward_rows,
                         backward, dq_rows,
                         probabilities, forward_bhnd, backward_bhnd, flops_forward,
-                        exact_causal_pairs, ForwardResult, BackwardResult)
+                        exact_causal_pairs, visible_pairs, CAUSAL_NONE, CAUSAL_TOP_LEFT,
+                        CAUSAL_BOTTOM_RIGHT, ForwardResult, BackwardResult)
 from .tiled import tiled_forward, tiled_ones
 
 __all__ = [
@@ -15,5 +16,6 @@ __all__ = [
     "scaled_scores", "row_max_and_repeats", "stable_shift", "forward", "forward_rows",
     "backward", "dq_rows",
     "probabilities", "forward_bhnd", "backward_bhnd", "flops_forward", "exact_causal_pairs",
+    "visible_pairs", "CAUSAL_NONE", "CAUSAL_TOP_LEFT", "CAUSAL_BOTTOM_RIGHT",
     "ForwardResult", "BackwardResult", "tiled_forward", "tiled_ones",
 ]

@@ -20,7 +20,9 @@ comparison and assignment operators):
     give m = beta * rm; rm < 0 and rs > 1 give m = 0; otherwise m = rm;
   * "mode 2" applies the same rule with the repeat count taken as at least 2, i.e. the shift
     is applied to every row whether or not a repeat has been seen yet;
-  * causal masking is top-left aligned: key j is visible to query i iff j <= i;
+  * causal masking is top-left aligned by default (key j visible to query i iff j <= i); the
+    bottom-right alignment (j <= i + Nk - Nq) is the other option, and a row that sees no key
+    has O = 0 and LSE = -inf (the log of an empty sum);
   * the saved logsumexp uses the natural log of the scaled scores: LSE = m + ln(l).
 """
 from __future__ import annotations
@@ -48,13 +50,33 @@ def bf16_round(x):
     return np.ldexp(np.rint(np.ldexp(mant, 8)), expo - 8)
 
 
-def visible(rows, n_keys, causal):
-    """Boolean [len(rows), n_keys]: key j is visible to query row i (top-left causal: j <= i)."""
+CAUSAL_NONE = 0
+CAUSAL_TOP_LEFT = 1
+CAUSAL_BOTTOM_RIGHT = 2
+
+
+def visible(rows, n_keys, causal, n_queries=None):
+    """Boolean [len(rows), n_keys]: whether key j is visible to query row i.
+
+    causal 0 / False: every key.  1 / True (top-left aligned): j <= i.  2 (bottom-right aligned,
+    the last query sees every key): j <= i + n_keys - n_queries, so with more queries than keys
+    the first n_queries - n_keys rows see no key at all.  n_queries is needed for 2 only; with
+    n_queries == n_keys the two alignments coincide.
+    """
     rows = np.asarray(rows)
     keys = np.arange(n_keys)
-    if not causal:
+    causal = int(causal)
+    if causal == CAUSAL_NONE:
         return np.ones((rows.size, n_keys), dtype=bool)
-    return keys[None, :] <= rows[:, None]
+    if causal == CAUSAL_TOP_LEFT:
+        off = 0
+    elif causal == CAUSAL_BOTTOM_RIGHT:
+        if n_queries is None:
+            raise ValueError("bottom-right alignment needs the number of queries")
+        off = n_keys - n_queries
+    else:
+        raise ValueError(f"causal must be 0, 1 or 2, got {causal}")
+    return keys[None, :] <= rows[:, None] + off
 
 
 def scaled_scores(q_rows, k, scale, mask):
@@ -69,10 +91,13 @@ def scaled_scores(q_rows, k, scale, mask):
 
 def row_max_and_repeats(s):
     """rm = rowmax(S) and rs = rowsum(S == rm): the repeated-maximum detection of [BF16-FA] §4.1
-    (the same statistic [BF16-FA] §7.1 suggests monitoring)."""
+    (the same statistic [BF16-FA] §7.1 suggests monitoring).  Visible scores are finite, so a row
+    with no visible key is the one whose max is -inf; it gets rs = 0."""
+    if s.shape[1] == 0:
+        return np.full(s.shape[0], -np.inf), np.zeros(s.shape[0], dtype=np.int64)
     rm = np.max(s, axis=1)
     rs = np.sum(s == rm[:, None], axis=1).astype(np.int64)
-    return rm, rs
+    return rm, np.where(rm == -np.inf, 0, rs)
 
 
 def stable_shift(rm, rs, beta, mode):
@@ -118,23 +143,28 @@ def forward_rows(q, k, v, rows, causal, scale, beta=1.25, mode=MODE_STANDARD):
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     rows = np.asarray(rows)
-    mask = visible(rows, k.shape[0], causal)
+    mask = visible(rows, k.shape[0], causal, q.shape[0])
     s = scaled_scores(q[rows], k, scale, mask)
     rm, rs = row_max_and_repeats(s)
-    m = stable_shift(rm, rs, beta, mode)
+    # A row with no visible key (bottom-right alignment with more queries than keys, or no keys)
+    # has the empty sum l = 0: O = 0 and LSE = ln 0 = -inf.  No shift applies to it; 0 is stored.
+    live = rm > -np.inf
+    m = np.where(live, stable_shift(np.where(live, rm, 0.0), rs, beta, mode), 0.0)
     p_hat = np.exp(s - m[:, None])  # exp(-inf) = 0 on invisible keys
     l = p_hat.sum(axis=1)
-    o = (p_hat @ v) / l[:, None]
-    lse = m + np.log(l)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        o = np.where(live[:, None], (p_hat @ v) / l[:, None], 0.0)
+        lse = np.where(live, m + np.log(l), -np.inf)
     ones = np.sum((bf16_round(p_hat) == 1.0) & mask, axis=1)
-    # The range of the softmax input, to be monitored ([FA-practice] §5): min over visible keys.
-    smin = np.min(np.where(mask, s, np.inf), axis=1)
+    # The range of the softmax input, to be monitored ([FA-practice] §5): min over visible keys
+    # (+inf for a row with none, the min of the empty set).
+    smin = np.min(np.where(mask, s, np.inf), axis=1, initial=np.inf)
     return ForwardResult(o, lse, rm, rs, m, l, ones, smin)
 
 
 def forward(q, k, v, causal, scale, beta=1.25, mode=MODE_STANDARD, row_chunk=1024):
-    """One head of attention: q [N, d], k [N, d], v [N, d] (float64): forward_rows over all rows,
-    in chunks of row_chunk rows to bound memory."""
+    """One head of attention: q [Nq, d], k [Nk, d], v [Nk, d] (float64): forward_rows over all
+    rows, in chunks of row_chunk rows to bound memory."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -157,9 +187,11 @@ def forward(q, k, v, causal, scale, beta=1.25, mode=MODE_STANDARD, row_chunk=102
 
 
 def probabilities(q_rows, k, scale, lse_rows, mask):
-    """Normalised P = exp(S - LSE) for a block of rows: the recomputation of [FA-backward] §2."""
+    """Normalised P = exp(S - LSE) for a block of rows: the recomputation of [FA-backward] §2.
+    Invisible entries are 0 (also in a row with no visible key, whose LSE is -inf)."""
     s = scaled_scores(q_rows, k, scale, mask)
-    return np.exp(s - lse_rows[:, None])
+    with np.errstate(invalid="ignore"):
+        return np.where(mask, np.exp(s - lse_rows[:, None]), 0.0)
 
 
 @dataclasses.dataclass
@@ -203,7 +235,7 @@ def backward(q, k, v, do, causal, scale, o=None, lse=None, row_chunk=1024):
 def _grad_rows(q, k, v, do, rows, causal, scale, lse_rows, delta_rows):
     """P and dS = P o (dP - delta), dP = dO V^T, for the query rows `rows` ([FA-backward] §2,
     [BF16-FA] §3.1)."""
-    mask = visible(rows, k.shape[0], causal)
+    mask = visible(rows, k.shape[0], causal, q.shape[0])
     p = probabilities(q[rows], k, scale, lse_rows, mask)
     dp = do[rows] @ v.T
     ds = p * (dp - delta_rows[:, None])
@@ -259,7 +291,7 @@ def backward_bhnd(q, k, v, do, causal, scale, heads=None, row_chunk=1024):
     """backward() over [B, H, N, d] arrays, restricted to `heads` if given."""
     q, k, v, do = _heads(q), _heads(k), _heads(v), _heads(do)
     B, H, N, d = q.shape
-    out = {name: np.zeros_like(q) for name in ("dq", "dk", "dv")}
+    out = {"dq": np.zeros_like(q), "dk": np.zeros_like(k), "dv": np.zeros_like(v)}
     out["delta"] = np.zeros((B, H, N))
     pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
     for b, h in pairs:
@@ -277,3 +309,13 @@ def flops_forward(B, H, N, d, causal):
 
 def exact_causal_pairs(N):
     return N * (N + 1) // 2
+
+
+def visible_pairs(Nq, Nk, causal):
+    """Number of (query, key) pairs visible under the mask `visible` defines, by summing the
+    per-row counts: min(Nk, max(0, i + off + 1)) for a causal alignment with offset off."""
+    causal = int(causal)
+    if causal == CAUSAL_NONE:
+        return Nq * Nk
+    off = 0 if causal == CAUSAL_TOP_LEFT else Nk - Nq
+    return sum(min(Nk, max(0, i + off + 1)) for i in range(Nq))

@@ -43,7 +43,7 @@ def tiled_forward(q, k, v, causal, scale, beta=1.25, mode=0, bc=64, order=None):
     if order is None:
         order = range(n_blocks)
     rows = np.arange(n)
-    mask_all = visible(rows, n_keys, causal)
+    mask_all = visible(rows, n_keys, causal, n)
 
     r = np.full(n, -np.inf)
     c = np.zeros(n, dtype=np.int64)
@@ -68,8 +68,10 @@ def tiled_forward(q, k, v, causal, scale, beta=1.25, mode=0, bc=64, order=None):
         acc = alpha[:, None] * acc + p_hat @ v[k0:k1]
         ones += np.sum((bf16_round(p_hat) == 1.0) & mask, axis=1)
         m = m_new
-    o = acc / l[:, None]
-    lse = m + np.log(l)
+    # A row with no visible key keeps l = 0: O = 0 and LSE = -inf.
+    with np.errstate(divide="ignore", invalid="ignore"):
+        o = np.where(l[:, None] > 0, acc / l[:, None], 0.0)
+        lse = np.where(l > 0, m + np.log(l), -np.inf)
     return {"o": o, "lse": lse, "r": r, "c": c, "m": m, "ones": ones}
 
 
@@ -92,7 +94,7 @@ def tiled_ones(q, k, causal, scale, beta=1.25, mode=0, bc=64, order=None):
     ones = np.zeros(n, dtype=np.int64)
     for j in order:
         k0, k1 = j * bc, min(n_keys, (j + 1) * bc)
-        mask = visible(rows, n_keys, causal)[:, k0:k1]
+        mask = visible(rows, n_keys, causal, n)[:, k0:k1]
         s = np.where(mask, scale * (q @ k[k0:k1].T), -np.inf)
         tm = np.max(s, axis=1)
         tc = np.sum((s == tm[:, None]) & mask, axis=1)

@@ -492,3 +492,160 @@ def test_row_subset_functions_match_full_oracle():
         dq, delta = oracle.dq_rows(q, k, v, do, rows, causal, 0.3)
         np.testing.assert_allclose(dq, br.dq[rows], rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(delta, br.delta[rows], rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------------------------
+# P11: Nq != Nk and the two causal alignments.  Top-left: query i sees keys j <= i.  Bottom-right:
+# the last query sees every key and each earlier query one key fewer, i.e. the query's distance
+# from the last query is at most the key's distance from the last key.  A query that sees no key
+# has the empty softmax sum: O = 0, LSE = -inf, zero gradients.
+
+
+def _sees(i, j, nq, nk, causal):
+    if causal == 0:
+        return True
+    if causal == 1:
+        return j <= i
+    return (nq - 1 - i) <= (nk - 1 - j)
+
+
+def _brute_force_rect(q, k, v, do, causal, scale):
+    """Scalar loops: O, LSE and, by the chain rule written per element, dQ, dK, dV."""
+    nq, nk, d, dv_ = len(q), len(k), len(q[0]), len(v[0])
+    o = [[0.0] * dv_ for _ in range(nq)]
+    lse = [-math.inf] * nq
+    dq = [[0.0] * d for _ in range(nq)]
+    dk = [[0.0] * d for _ in range(nk)]
+    dv = [[0.0] * dv_ for _ in range(nk)]
+    for i in range(nq):
+        keys = [j for j in range(nk) if _sees(i, j, nq, nk, causal)]
+        if not keys:
+            continue
+        e = {j: math.exp(scale * sum(q[i][c] * k[j][c] for c in range(d))) for j in keys}
+        z = sum(e.values())
+        lse[i] = math.log(z)
+        p = {j: e[j] / z for j in keys}
+        for c in range(dv_):
+            o[i][c] = sum(p[j] * v[j][c] for j in keys)
+        # dL/dp_j = do_i . v_j; softmax Jacobian: dS_j = p_j (dL/dp_j - sum_l p_l dL/dp_l)
+        g = {j: sum(do[i][c] * v[j][c] for c in range(dv_)) for j in keys}
+        gbar = sum(p[j] * g[j] for j in keys)
+        for j in keys:
+            ds = p[j] * (g[j] - gbar)
+            for c in range(d):
+                dq[i][c] += scale * ds * k[j][c]
+                dk[j][c] += scale * ds * q[i][c]
+            for c in range(dv_):
+                dv[j][c] += p[j] * do[i][c]
+    return tuple(np.array(x) for x in (o, lse, dq, dk, dv))
+
+
+@pytest.mark.parametrize("causal", [0, 1, 2])
+@pytest.mark.parametrize("nq,nk", [(3, 7), (7, 3), (1, 5), (5, 1), (6, 6), (9, 4)])
+def test_brute_force_rectangular(causal, nq, nk):
+    rng = np.random.default_rng(100 * nq + nk + causal)
+    d = 4
+    q, do = rng.standard_normal((nq, d)), rng.standard_normal((nq, d))
+    k, v = rng.standard_normal((nk, d)), rng.standard_normal((nk, d))
+    o, lse, dq, dk, dv = _brute_force_rect(q.tolist(), k.tolist(), v.tolist(), do.tolist(), causal, 0.6)
+    for mode in (0, 1, 2):
+        fr = oracle.forward(q, k, v, causal, 0.6, BETA, mode)
+        np.testing.assert_allclose(fr.o, o, rtol=1e-12, atol=1e-12)
+        assert np.array_equal(np.isinf(fr.lse), np.isinf(lse))
+        fin = np.isfinite(lse)
+        np.testing.assert_allclose(fr.lse[fin], lse[fin], rtol=1e-12, atol=1e-12)
+        assert np.all(fr.lse[~fin] == -np.inf)
+        tr = oracle.tiled_forward(q, k, v, causal, 0.6, BETA, mode, bc=2)
+        np.testing.assert_allclose(tr["o"], o, rtol=1e-12, atol=1e-12)
+        assert np.array_equal(tr["lse"][~fin], lse[~fin])
+    br = oracle.backward(q, k, v, do, causal, 0.6)
+    np.testing.assert_allclose(br.dq, dq, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(br.dk, dk, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(br.dv, dv, rtol=1e-10, atol=1e-12)
+    vis = oracle.visible(np.arange(nq), nk, causal, nq)
+    assert int(vis.sum()) == oracle.visible_pairs(nq, nk, causal)
+    for i in range(nq):
+        for j in range(nk):
+            assert vis[i, j] == _sees(i, j, nq, nk, causal)
+
+
+def test_bottom_right_is_the_tail_of_a_square_problem():
+    """Bottom-right with Nq < Nk: the queries sit at the last Nq positions of an Nk x Nk causal
+    problem.  O, LSE and the counts equal that problem's last rows; dK and dV equal its
+    gradients when the first Nk - Nq rows carry no output gradient."""
+    rng = np.random.default_rng(8)
+    nk, nq, d = 45, 13, 8
+    qf, kf, vf, dof = (rng.standard_normal((nk, d)) for _ in range(4))
+    kf[30] = kf[7]
+    qf[40] = kf[7]
+    dof[: nk - nq] = 0.0
+    for mode in (0, 1, 2):
+        sq = oracle.forward(qf, kf, vf, True, 0.4, BETA, mode)
+        br = oracle.forward(qf[nk - nq:], kf, vf, 2, 0.4, BETA, mode)
+        for name in ("o", "lse", "rm", "rs", "m", "l", "ones", "smin"):
+            np.testing.assert_array_equal(getattr(br, name), getattr(sq, name)[nk - nq:], err_msg=name)
+    gs = oracle.backward(qf, kf, vf, dof, True, 0.4)
+    gb = oracle.backward(qf[nk - nq:], kf, vf, dof[nk - nq:], 2, 0.4)
+    np.testing.assert_allclose(gb.dq, gs.dq[nk - nq:], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(gb.dk, gs.dk, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(gb.dv, gs.dv, rtol=1e-12, atol=1e-13)
+    # and it differs from top-left on the same rectangular problem
+    tl = oracle.forward(qf[nk - nq:], kf, vf, 1, 0.4)
+    assert not np.allclose(tl.o, oracle.forward(qf[nk - nq:], kf, vf, 2, 0.4).o)
+
+
+def test_more_queries_than_keys():
+    """Nq > Nk.  Top-left: rows from Nk - 1 on see every key (the non-causal result).
+    Bottom-right: the first Nq - Nk rows see nothing (O = 0, LSE = -inf, no gradient); the rest
+    are the Nk x Nk causal problem of those rows."""
+    rng = np.random.default_rng(9)
+    nq, nk, d = 21, 8, 8
+    q, do = rng.standard_normal((nq, d)), rng.standard_normal((nq, d))
+    k, v = rng.standard_normal((nk, d)), rng.standard_normal((nk, d))
+    tl = oracle.forward(q, k, v, 1, 0.5)
+    full = oracle.forward(q, k, v, 0, 0.5)
+    np.testing.assert_array_equal(tl.o[nk - 1:], full.o[nk - 1:])
+    np.testing.assert_array_equal(tl.lse[nk - 1:], full.lse[nk - 1:])
+    e = nq - nk
+    brf = oracle.forward(q, k, v, 2, 0.5, BETA, 2)
+    assert np.all(brf.o[:e] == 0) and np.all(brf.lse[:e] == -np.inf) and np.all(brf.l[:e] == 0)
+    assert np.all(brf.rs[:e] == 0) and np.all(brf.ones[:e] == 0) and np.all(brf.smin[:e] == np.inf)
+    assert np.all(brf.rm[:e] == -np.inf)
+    sq = oracle.forward(q[e:], k, v, 1, 0.5, BETA, 2)
+    np.testing.assert_array_equal(brf.o[e:], sq.o)
+    np.testing.assert_array_equal(brf.lse[e:], sq.lse)
+    gb = oracle.backward(q, k, v, do, 2, 0.5)
+    gs = oracle.backward(q[e:], k, v, do[e:], 1, 0.5)
+    assert np.all(gb.dq[:e] == 0) and np.all(gb.delta[:e] == 0)
+    np.testing.assert_allclose(gb.dq[e:], gs.dq, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(gb.dk, gs.dk, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(gb.dv, gs.dv, rtol=1e-12, atol=1e-13)
+
+
+def test_no_keys_and_single_query():
+    rng = np.random.default_rng(10)
+    q, do = rng.standard_normal((5, 4)), rng.standard_normal((5, 4))
+    k = v = np.zeros((0, 4))
+    for causal in (0, 1, 2):
+        fr = oracle.forward(q, k, v, causal, 0.5, BETA, 1)
+        assert np.all(fr.o == 0) and np.all(fr.lse == -np.inf)
+        br = oracle.backward(q, k, v, do, causal, 0.5)
+        assert br.dq.shape == (5, 4) and np.all(br.dq == 0) and br.dk.shape == (0, 4)
+    # one query, bottom-right: it sees every key, so the result is the non-causal one
+    k, v = rng.standard_normal((9, 4)), rng.standard_normal((9, 4))
+    a = oracle.forward(q[:1], k, v, 2, 0.5)
+    b = oracle.forward(q[:1], k, v, 0, 0.5)
+    np.testing.assert_array_equal(a.o, b.o)
+    assert oracle.visible_pairs(1, 9, 1) == 1 and oracle.visible_pairs(1, 9, 2) == 9
+
+
+def test_visible_pairs_closed_forms():
+    for nq, nk in [(8192, 8192), (100, 300), (300, 100), (1, 1), (0, 5), (5, 0)]:
+        assert oracle.visible_pairs(nq, nk, 0) == nq * nk
+        if nq <= nk:
+            assert oracle.visible_pairs(nq, nk, 1) == nq * (nq + 1) // 2
+            assert oracle.visible_pairs(nq, nk, 2) == nq * nk - nq * (nq - 1) // 2
+        else:
+            assert oracle.visible_pairs(nq, nk, 1) == nk * (nk + 1) // 2 + (nq - nk) * nk
+            assert oracle.visible_pairs(nq, nk, 2) == nk * (nk + 1) // 2
+    assert oracle.visible_pairs(8192, 8192, 1) == oracle.exact_causal_pairs(8192)
