@@ -57,7 +57,7 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = 1,    /* a required pointer is NULL */
-  FA_ERR_SHAPE = 2,   /* B, H or N negative, or the problem too large */
+  FA_ERR_SHAPE = 2,   /* B, H or a sequence length negative, or the problem too large */
   FA_ERR_HEADDIM = 3, /* d is not 64 or 128 */
   FA_ERR_PARAM = 4,   /* causal, scale, beta or stable_flag out of range */
   FA_ERR_ALIGN = 5,   /* a pointer is not aligned as stated above */
@@ -102,6 +102,27 @@ int fa_fwd_stats(const void* q, const void* k, const void* v, void* o, float* ls
                  int B, int H, int N, int d, int causal, float scale, float beta, int stable_flag,
                  int flags, void* stream);
 
+/* Forward pass over Nq queries and Nk keys per head (every other convention as above):
+ *   q, o        [B,H,Nq,d] bf16;  k, v [B,H,Nk,d] bf16;  lse and every diagnostic [B,H,Nq];
+ *   causal      FA_CAUSAL_NONE (0), FA_CAUSAL_TOP_LEFT (1: key j visible to query i iff j <= i)
+ *               or FA_CAUSAL_BOTTOM_RIGHT (2: iff j <= i + Nk - Nq, so the last query sees every
+ *               key, the alignment of a query block appended to a longer key sequence);
+ *   Nq, Nk >= 0, each independently ragged (no tile multiple needed).
+ * The tile boundaries at the sequence ends follow the ijyty.com article §4.2 (a block's extent is
+ * clipped to what is left of the sequence); a query block attending to a longer key sequence is
+ * the generation setting its §6.1 extends the method to.  A query that sees no key (Nk == 0, or
+ * bottom-right with i < Nq - Nk) gets O = 0, lse = -inf, dupcnt = ones = 0, smin = +inf,
+ * smax = -inf.  With Nq == Nk both causal alignments equal fa_fwd_stats's causal = 1.
+ * Empty problems (B*H == 0 or Nq == 0) are no-ops; k and v may be NULL when Nk == 0.
+ * Errors as fa_fwd_stats; causal outside 0..2 -> FA_ERR_PARAM. */
+#define FA_CAUSAL_NONE 0
+#define FA_CAUSAL_TOP_LEFT 1
+#define FA_CAUSAL_BOTTOM_RIGHT 2
+int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse,
+              int32_t* dupcnt, int32_t* ones, float* smin, float* smax,
+              int B, int H, int Nq, int Nk, int d, int causal, float scale, float beta,
+              int stable_flag, int flags, void* stream);
+
 /* Backward pass: from q, k, v, the forward's o and lse, and the upstream gradient dO, writes
  * dq, dk, dv [B,H,N,d] bf16.  delta_ws is a caller-owned fp32 workspace of
  * fa_bwd_workspace_bytes(B,H,N,d) bytes; on return (in stream order) it holds
@@ -128,12 +149,23 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
               int B, int H, int N, int d, int causal, float scale, float beta, int stable_flag,
               int stages, void* stream);
 
-/* Bytes of the delta workspace fa_bwd needs: B*H*N*4 (0 for invalid or empty shapes). */
+/* Backward pass over Nq queries and Nk keys per head, as fa_bwd_ex with the shapes and causal
+ * alignments of fa_fwd_qk: dq, dO, o [B,H,Nq,d]; dk, dv [B,H,Nk,d]; lse, delta_ws [B,H,Nq].  A
+ * query that sees no key contributes nothing (its dq row is 0); a key that no query sees gets
+ * dk = dv = 0.  No-op when B*H == 0 or Nq == Nk == 0.  Pointers of tensors with no elements
+ * (the Nk-sized ones when Nk == 0, the Nq-sized ones when Nq == 0) may be NULL. */
+int fa_bwd_qk(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dO, void* dq, void* dk, void* dv, float* delta_ws,
+              int B, int H, int Nq, int Nk, int d, int causal, float scale, float beta,
+              int stable_flag, int stages, void* stream);
+
+/* Bytes of the delta workspace fa_bwd needs: B*H*N*4 (0 for invalid or empty shapes); for
+ * fa_bwd_qk pass N = Nq. */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 
 /* Width of the key blocks the forward processes per step for head dimension d and the given
- * causal flag (0 if d is not supported): the granularity at which the running maximum, repeat
- * count and shift change. */
+ * causal flag (any non-zero alignment counts as causal; 0 if d is not supported): the
+ * granularity at which the running maximum, repeat count and shift change. */
 int fa_fwd_kv_block(int d, int causal);
 
 /* Measurement helper, not part of the attention path: runs n_workgroups workgroups of 256

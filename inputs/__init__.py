@@ -4,6 +4,8 @@ This package holds no attention arithmetic: it only draws random tensors and app
 input constructions (duplicated key rows, an attention-sink key, a value grid) that the
 workloads call for.
 """
-from .gen import CONFIGS, WorkloadConfig, make_inputs, randn_inputs, grid_inputs, tensor_digest
+from .gen import (CONFIGS, WorkloadConfig, make_inputs, randn_inputs, grid_inputs, rect_inputs,
+                  tensor_digest)
 
-__all__ = ["CONFIGS", "WorkloadConfig", "make_inputs", "randn_inputs", "grid_inputs", "tensor_digest"]
+__all__ = ["CONFIGS", "WorkloadConfig", "make_inputs", "randn_inputs", "grid_inputs", "rect_inputs",
+           "tensor_digest"]

@@ -87,6 +87,20 @@ def randn_inputs(B, H, N, d, seed, sigma_qk=1.0):
     return {"q": q, "k": k, "v": v, "do": do}
 
 
+def rect_inputs(B, H, Nq, Nk, d, seed, grid=False):
+    """Q and dO [B, H, Nq, d], K and V [B, H, Nk, d] for a query block attending to a key sequence
+    of another length (drawn in the order Q, K, V, dO).  Q, K ~ N(0, 1), or uniform over
+    GRID_VALUES with grid=True; V, dO ~ N(0, 1)."""
+    g = _gen(seed)
+    qs, ks = (B, H, Nq, d), (B, H, Nk, d)
+    draw = _grid_bf16 if grid else _randn_bf16
+    q = draw(g, qs)
+    k = draw(g, ks)
+    v = _randn_bf16(g, ks)
+    do = _randn_bf16(g, qs)
+    return {"q": q, "k": k, "v": v, "do": do}
+
+
 def grid_inputs(B, H, N, d, seed):
     """Q, K uniform over GRID_VALUES (exact ties in row maxima are frequent); V, dO ~ N(0, 1)."""
     g = _gen(seed)

@@ -18,28 +18,25 @@ constexpr int64_t kMaxElems = int64_t(1) << 40;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// Shared shape/parameter checks.  Returns FA_OK, or the first error found.  *empty is set when
-// the problem has no rows (a successful no-op).
-int check_common(int B, int H, int N, int d, int causal, float scale, float beta, int stable_flag,
-                 bool* empty) {
-  *empty = false;
-  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+// Shared shape/parameter checks.  Returns FA_OK, or the first error found.
+int check_common(int B, int H, int Nq, int Nk, int d, int causal, float scale, float beta, int stable_flag) {
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
-  if (causal != 0 && causal != 1) return FA_ERR_PARAM;
+  if (causal < FA_CAUSAL_NONE || causal > FA_CAUSAL_BOTTOM_RIGHT) return FA_ERR_PARAM;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_PARAM;
   if (!std::isfinite(beta) || !(beta >= 1.f)) return FA_ERR_PARAM;
   if (stable_flag < 0 || stable_flag > 2) return FA_ERR_PARAM;
-  const int64_t rows = int64_t(B) * int64_t(H) * int64_t(N);
-  if (rows == 0) {
-    *empty = true;
-    return FA_OK;
-  }
-  if (int64_t(B) * int64_t(H) > INT32_MAX / 8) return FA_ERR_SHAPE;
-  if (rows * d >= kMaxElems) return FA_ERR_SHAPE;
+  const int64_t bh = int64_t(B) * int64_t(H);
+  if (bh == 0) return FA_OK;
+  if (bh > INT32_MAX / 8) return FA_ERR_SHAPE;
+  if (bh * Nq * d >= kMaxElems || bh * Nk * d >= kMaxElems) return FA_ERR_SHAPE;
   // One head's rows are addressed through 32-bit buffer ranges.
-  if (int64_t(N) * d * 2 > int64_t(INT32_MAX)) return FA_ERR_SHAPE;
+  if (int64_t(Nq) * d * 2 > int64_t(INT32_MAX) || int64_t(Nk) * d * 2 > int64_t(INT32_MAX)) return FA_ERR_SHAPE;
   return FA_OK;
 }
+
+// Key j is visible to query i iff j <= i + coff.
+int causal_offset(int causal, int Nq, int Nk) { return causal == FA_CAUSAL_BOTTOM_RIGHT ? Nk - Nq : 0; }
 
 int hip_status(hipError_t e) {
   if (e == hipSuccess) return FA_OK;
@@ -51,15 +48,15 @@ int hip_status(hipError_t e) {
 
 extern "C" {
 
-int fa_fwd_stats(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* dupcnt,
-                 int32_t* ones, float* smin, float* smax, int B, int H, int N, int d, int causal,
-                 float scale, float beta, int stable_flag, int flags, void* stream) {
-  bool empty = false;
-  const int st = check_common(B, H, N, d, causal, scale, beta, stable_flag, &empty);
+int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* dupcnt,
+              int32_t* ones, float* smin, float* smax, int B, int H, int Nq, int Nk, int d, int causal,
+              float scale, float beta, int stable_flag, int flags, void* stream) {
+  const int st = check_common(B, H, Nq, Nk, d, causal, scale, beta, stable_flag);
   if (st != FA_OK) return st;
   if ((flags & ~FA_FWD_COMPENSATED_SUM) != 0) return FA_ERR_PARAM;
-  if (empty) return FA_OK;
-  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (int64_t(B) * H == 0 || Nq == 0) return FA_OK;
+  if (!q || !o || !lse) return FA_ERR_NULL;
+  if (Nk > 0 && (!k || !v)) return FA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return FA_ERR_ALIGN;
   if (!aligned(lse, 4) || (dupcnt && !aligned(dupcnt, 4)) || (ones && !aligned(ones, 4))) return FA_ERR_ALIGN;
   if ((smin && !aligned(smin, 4)) || (smax && !aligned(smax, 4))) return FA_ERR_ALIGN;
@@ -75,7 +72,9 @@ int fa_fwd_stats(const void* q, const void* k, const void* v, void* o, float* ls
   a.smin = smin;
   a.smax = smax;
   a.BH = B * H;
-  a.N = N;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.coff = causal_offset(causal, Nq, Nk);
   a.sl2 = scale * 1.4426950408889634f;
   a.scale = scale;
   a.beta = beta;
@@ -83,6 +82,14 @@ int fa_fwd_stats(const void* q, const void* k, const void* v, void* o, float* ls
   const bool kahan = (flags & FA_FWD_COMPENSATED_SUM) != 0;
   return hip_status(
       fa::launch_fwd(a, d, causal != 0, stable_flag, stats, kahan, static_cast<hipStream_t>(stream)));
+}
+
+int fa_fwd_stats(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* dupcnt,
+                 int32_t* ones, float* smin, float* smax, int B, int H, int N, int d, int causal,
+                 float scale, float beta, int stable_flag, int flags, void* stream) {
+  if (causal != 0 && causal != 1) return FA_ERR_PARAM;
+  return fa_fwd_qk(q, k, v, o, lse, dupcnt, ones, smin, smax, B, H, N, N, d, causal, scale, beta,
+                   stable_flag, flags, stream);
 }
 
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* dupcnt,
@@ -98,15 +105,17 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
                    stream);
 }
 
-int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
-              const void* dO, void* dq, void* dk, void* dv, float* delta_ws, int B, int H, int N,
+int fa_bwd_qk(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dO, void* dq, void* dk, void* dv, float* delta_ws, int B, int H, int Nq, int Nk,
               int d, int causal, float scale, float beta, int stable_flag, int stages, void* stream) {
-  bool empty = false;
-  const int st = check_common(B, H, N, d, causal, scale, beta, stable_flag, &empty);
+  const int st = check_common(B, H, Nq, Nk, d, causal, scale, beta, stable_flag);
   if (st != FA_OK) return st;
   if (stages < 1 || stages > FA_BWD_ALL) return FA_ERR_PARAM;
-  if (empty) return FA_OK;
-  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !delta_ws) return FA_ERR_NULL;
+  if (int64_t(B) * H == 0 || (Nq == 0 && Nk == 0)) return FA_OK;
+  if (Nq > 0 && (!q || !o || !lse || !dO || !dq || !delta_ws)) return FA_ERR_NULL;
+  if (Nk > 0 && (!k || !v || !dk || !dv)) return FA_ERR_NULL;
+  // dK and dV read Q, dO, LSE and delta whenever there are queries at all.
+  if (Nq > 0 && Nk > 0 && (!q || !dO)) return FA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dO, 16) ||
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
     return FA_ERR_ALIGN;
@@ -124,7 +133,9 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
   a.dv = static_cast<uint16_t*>(dv);
   a.delta = delta_ws;
   a.BH = B * H;
-  a.N = N;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.coff = causal_offset(causal, Nq, Nk);
   a.scale = scale;
   a.sl2 = scale * 1.4426950408889634f;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -139,6 +150,14 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
   }
   if (stages & FA_BWD_DQ) rc = hip_status(fa::launch_bwd_dq(a, d, causal != 0, s));
   return rc;
+}
+
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dO, void* dq, void* dk, void* dv, float* delta_ws, int B, int H, int N,
+              int d, int causal, float scale, float beta, int stable_flag, int stages, void* stream) {
+  if (causal != 0 && causal != 1) return FA_ERR_PARAM;
+  return fa_bwd_qk(q, k, v, o, lse, dO, dq, dk, dv, delta_ws, B, H, N, N, d, causal, scale, beta,
+                   stable_flag, stages, stream);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -166,7 +185,7 @@ const char* fa_status_str(int status) {
   switch (status) {
     case FA_OK: return "FA_OK";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
-    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: B, H or N negative, or the problem is too large";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: B, H or a sequence length negative, or the problem is too large";
     case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: d must be 64 or 128";
     case FA_ERR_PARAM: return "FA_ERR_PARAM: causal, scale, beta or stable_flag out of range";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensor pointers must be 16-byte aligned, vectors 4-byte";

@@ -29,7 +29,7 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(BwdArgs a) {
   constexpr int TPR = D / 8;
   constexpr int RPB = kThreads / TPR;
   const int tid = threadIdx.x;
-  const int64_t total = (int64_t)a.BH * a.N;
+  const int64_t total = (int64_t)a.BH * a.Nq;
   const int64_t row = (int64_t)blockIdx.x * RPB + tid / TPR;
   const int c = tid % TPR;
   float acc = 0.f;
@@ -79,7 +79,7 @@ __device__ __forceinline__ void dq_sdp(const uint16_t* tK, const uint16_t* tV, i
 }
 
 template <bool MASK, bool CAUSAL>
-__device__ __forceinline__ void dq_grad(const f32x16& s, const f32x16& dp, int key0, int qrow, int N, int hh,
+__device__ __forceinline__ void dq_grad(const f32x16& s, const f32x16& dp, int key0, int qrow, int nk, int hh,
                                         float sl2, float lse2, float dlt, uint32_t (&pds)[8]) {
 #pragma unroll
   for (int r = 0; r < 16; r += 2) {
@@ -89,9 +89,11 @@ __device__ __forceinline__ void dq_grad(const f32x16& s, const f32x16& dp, int k
       const int rr = r + u;
       float p = fast_exp2(fmaf(s[rr], sl2, -lse2));
       if (MASK) {
-        // Key key0 + c + 4 hh, c = 8 (rr / 4) + rr % 4, is hidden past N or (causal) past the
-        // lane's query: c > lim.
-        const int lim = min(CAUSAL ? qrow - key0 - 4 * hh : INT_MAX, N - 1 - key0 - 4 * hh);
+        // Key indices here are relative to the causal offset (key0 = block start - coff,
+        // nk = Nk - coff).  Key key0 + c + 4 hh, c = 8 (rr / 4) + rr % 4, is hidden past the last
+        // key or (causal) past the lane's query: c > lim.  The select also clears the infinite p
+        // of a query that sees no key (LSE = -inf).
+        const int lim = min(CAUSAL ? qrow - key0 - 4 * hh : INT_MAX, nk - 1 - key0 - 4 * hh);
         const int c = 8 * (rr >> 2) + (rr & 3);
         p = (c > lim) ? 0.f : p;
       }
@@ -131,30 +133,31 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
   int bh, rank;
   map_block(blockIdx.x, a.BH, a.n_tiles, bh, rank);
   const int qt = CAUSAL ? a.n_tiles - 1 - rank : rank;
-  const int N = a.N;
+  const int Nq = a.Nq, Nk = a.Nk;
   const int q0 = qt * BR;
-  const int64_t hoff = (int64_t)bh * N * D;
-  const uint16_t* Kg = a.k + hoff;
-  const uint16_t* Vg = a.v + hoff;
+  const int64_t qoff = (int64_t)bh * Nq * D;
+  const int64_t koff = (int64_t)bh * Nk * D;
+  const uint16_t* Kg = a.k + koff;
+  const uint16_t* Vg = a.v + koff;
   const int qrow = q0 + wave * 32 + l32;
-  const int qsrc = min(qrow, N - 1);
+  const int qsrc = min(qrow, Nq - 1);
 
   bf16x8 qf[KS], gf[KS];
   {
-    const uint16_t* qs = a.q + hoff + (int64_t)qsrc * D + 8 * hh;
-    const uint16_t* gs = a.dO + hoff + (int64_t)qsrc * D + 8 * hh;
+    const uint16_t* qs = a.q + qoff + (int64_t)qsrc * D + 8 * hh;
+    const uint16_t* gs = a.dO + qoff + (int64_t)qsrc * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qf[ks] = as_bf16x8(*reinterpret_cast<const i32x4*>(qs + 16 * ks));
       gf[ks] = as_bf16x8(*reinterpret_cast<const i32x4*>(gs + 16 * ks));
     }
   }
-  const float lse2 = a.lse[(int64_t)bh * N + qsrc] * kLog2e;
-  const float dlt = a.delta[(int64_t)bh * N + qsrc];
+  const float lse2 = a.lse[(int64_t)bh * Nq + qsrc] * kLog2e;
+  const float dlt = a.delta[(int64_t)bh * Nq + qsrc];
 
-  int n_kv = (N + BC - 1) / BC;
-  if (CAUSAL) n_kv = min(n_kv, (q0 + BR - 1) / BC + 1);
-  const int n_plain = min(n_kv, CAUSAL ? q0 / BC : N / BC);
+  int n_kv = (Nk + BC - 1) / BC;
+  if (CAUSAL) n_kv = min(n_kv, blocks_through(q0 + BR - 1 + a.coff, BC));
+  const int n_plain = min(n_kv, CAUSAL ? min(blocks_within(q0 + a.coff, BC), Nk / BC) : Nk / BC);
 
   f32x16 acc[DT];
 #pragma unroll
@@ -168,8 +171,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
   st.init(tid);
   constexpr uint32_t kTileBytes = BC * D * 2;
   const uint32_t aK = lds_addr(&sK[0][0]), aV = lds_addr(&sV[0][0]);
-  st.issue(Kg, 0, N, aK + p0 * kTileBytes);
-  st.issue(Vg, 0, N, aV + p0 * kTileBytes);
+  st.issue(Kg, 0, Nk, aK + p0 * kTileBytes);
+  st.issue(Vg, 0, Nk, aV + p0 * kTileBytes);
   wait_vm0();
   __syncthreads();
 
@@ -179,8 +182,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
     constexpr int buf = decltype(buf_tag)::value;
     const int kv0 = j * BC;
     if (j + 1 < n_kv) {
-      st.issue(Kg, kv0 + BC, N, aK + (buf ^ 1) * kTileBytes);
-      st.issue(Vg, kv0 + BC, N, aV + (buf ^ 1) * kTileBytes);
+      st.issue(Kg, kv0 + BC, Nk, aK + (buf ^ 1) * kTileBytes);
+      st.issue(Vg, kv0 + BC, Nk, aV + (buf ^ 1) * kTileBytes);
     }
     const uint16_t* tK = sK[buf];
     const uint16_t* tV = sV[buf];
@@ -193,10 +196,10 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     // dS of the first half on the vector ALUs while the second half's S/dP run on the matrix cores.
     dq_sdp<D>(tK, tV, 32, l32, hh, qf, gf, s1, dp1);
-    dq_grad<MASK, CAUSAL>(s, dp, kv0, qrow, N, hh, a.sl2, lse2, dlt, pds0);
+    dq_grad<MASK, CAUSAL>(s, dp, kv0 - a.coff, qrow, Nk - a.coff, hh, a.sl2, lse2, dlt, pds0);
     sched_reads_ahead_valu<2 * KS, 1, 4, 4>();
     __builtin_amdgcn_sched_barrier(0);
-    dq_grad<MASK, CAUSAL>(s1, dp1, kv0 + 32, qrow, N, hh, a.sl2, lse2, dlt, pds1);
+    dq_grad<MASK, CAUSAL>(s1, dp1, kv0 + 32 - a.coff, qrow, Nk - a.coff, hh, a.sl2, lse2, dlt, pds1);
     dq_accum<D>(tK, 0, lane, pds0, acc);
     sched_reads_ahead_valu<2 * DT, 2, 3, 8>();
     __builtin_amdgcn_sched_barrier(0);
@@ -221,8 +224,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
     if (j < n_kv) step(masked{}, buf1{});
   }
 
-  if (qrow < N) {
-    uint16_t* dst = a.dq + hoff + (int64_t)qrow * D;
+  if (qrow < Nq) {
+    uint16_t* dst = a.dq + qoff + (int64_t)qrow * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -313,7 +316,7 @@ struct DkvSched {
 // order the instructions issue in.
 template <int D, bool CAUSAL, bool MASK>
 __device__ __forceinline__ void dkdv_block(const uint16_t* tQ, const uint16_t* tG, const float* tL,
-                                           const float* tD, int q0, int N, int key, int lane, float sl2,
+                                           const float* tD, int q0, int Nq, int coff, int key, int lane, float sl2,
                                            const DkvFrags<D>& f, f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
   using S = DkvSched<D>;
   constexpr int DT = D / 32;
@@ -369,7 +372,8 @@ __device__ __forceinline__ void dkdv_block(const uint16_t* tQ, const uint16_t* t
     }
   };
   // Element e of half g: P = exp2(S scale log2e - LSE log2e), dS = P (dP - delta), masked queries
-  // (past N, or before this lane's key when causal) give zero; pairs are packed to bf16.
+  // (past Nq, or, when causal, before key - coff, the first query that sees this lane's key)
+  // give zero; pairs are packed to bf16.
   auto grad_elem = [&](auto mc) __attribute__((always_inline)) {
     constexpr int m = decltype(mc)::value;
     constexpr int g = m >> 3, e = m & 7;
@@ -381,10 +385,11 @@ __device__ __forceinline__ void dkdv_block(const uint16_t* tQ, const uint16_t* t
     const float dl = u == 0 ? d4.x : u == 1 ? d4.y : u == 2 ? d4.z : d4.w;
     float p = fast_exp2(fmaf(s[c][r], sl2, -lv));
     if (MASK) {
-      // Query q0 + c + 4 hh, c = 32 t + 8 rq + u, is hidden past N or (causal) before this
-      // lane's key: c > hi or c < lo.
-      const int hi = N - 1 - q0 - 4 * hh;
-      const int lo = CAUSAL ? key - q0 - 4 * hh : INT_MIN;
+      // Query q0 + c + 4 hh, c = 32 t + 8 rq + u, is hidden past Nq or (causal) before
+      // key - coff: c > hi or c < lo.  The select also clears the infinite p of a query that sees
+      // no key.
+      const int hi = Nq - 1 - q0 - 4 * hh;
+      const int lo = CAUSAL ? key - (q0 + coff) - 4 * hh : INT_MIN;
       constexpr int c = 32 * t + 8 * rq + u;
       p = (c > hi || c < lo) ? 0.f : p;
     }
@@ -432,20 +437,21 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   int bh, rank;
   map_block(blockIdx.x, a.BH, a.n_tiles, bh, rank);
   const int kt = rank;  // causal: the first key tiles see the most queries, so they start first
-  const int N = a.N;
+  const int Nq = a.Nq, Nk = a.Nk;
   const int k0 = kt * BK;
-  const int64_t hoff = (int64_t)bh * N * D;
-  const int64_t roff = (int64_t)bh * N;
-  const uint16_t* Qg = a.q + hoff;
-  const uint16_t* Gg = a.dO + hoff;
+  const int64_t qoff = (int64_t)bh * Nq * D;
+  const int64_t koff = (int64_t)bh * Nk * D;
+  const int64_t roff = (int64_t)bh * Nq;
+  const uint16_t* Qg = a.q + qoff;
+  const uint16_t* Gg = a.dO + qoff;
   const int kw0 = k0 + wave * 32;
   const int key = kw0 + l32;
-  const int ksrc = min(key, N - 1);
+  const int ksrc = min(key, Nk - 1);
 
   DkvFrags<D> f;
   {
-    const uint16_t* ks_ = a.k + hoff + (int64_t)ksrc * D + 8 * hh;
-    const uint16_t* vs_ = a.v + hoff + (int64_t)ksrc * D + 8 * hh;
+    const uint16_t* ks_ = a.k + koff + (int64_t)ksrc * D + 8 * hh;
+    const uint16_t* vs_ = a.v + koff + (int64_t)ksrc * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       f.k[ks] = as_bf16x8(*reinterpret_cast<const i32x4*>(ks_ + 16 * ks));
@@ -453,8 +459,12 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
     }
   }
 
-  const int n_q = (N + BQ - 1) / BQ;
-  const int i_first = CAUSAL ? (k0 / BQ) : 0;
+  // Query blocks visited: i_first .. n_q - 1 (causal: from the block of the first query that
+  // sees key k0).  Causal blocks before i_lead hold queries that do not see every key of the
+  // tile (those before k0 + BK - 1 - coff) and need the mask.
+  const int n_q = (Nq + BQ - 1) / BQ;
+  const int i_first = CAUSAL ? max(0, k0 - a.coff) / BQ : 0;
+  const int i_lead = CAUSAL ? min(n_q, blocks_through(k0 + BK - 2 - a.coff, BQ)) : 0;
 
   f32x16 dk[DT], dv[DT];
 #pragma unroll
@@ -470,7 +480,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   float vl = 0.f, vd = 0.f;
   auto load_rows = [&](int i) __attribute__((always_inline)) {
     if (tid < BQ) {
-      const int64_t src = roff + min(i * BQ + tid, N - 1);
+      const int64_t src = roff + min(i * BQ + tid, Nq - 1);
       vl = a.lse[src];  // scaled when stored: no arithmetic here, so nothing waits for the load
       vd = a.delta[src];
     }
@@ -482,11 +492,9 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
     }
   };
 
-  // Blocks are visited in order i_first .. n_q - 1.  Only two of them can need masking: the
-  // causal diagonal block (the first, since key and query tiles have the same height) and a
-  // ragged last block.  They run through the masked body outside the main loop, so the loop body
-  // has a single variant and the accumulators need no copies at branch joins.
-  static_assert(kDkvBq == kDkvBk, "the diagonal block must be the first block");
+  // The masked blocks (the causal leading ones, one or two of them, and a ragged last block) run
+  // through the masked body outside the main loop, so the loop body has a single variant and
+  // the accumulators need no copies at branch joins.
   int i = i_first;
   int buf = 0;
   auto step = [&](auto mask_tag) __attribute__((always_inline)) {
@@ -494,11 +502,11 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
     const int q0 = i * BQ;
     const bool has_next = (i + 1 < n_q);
     if (has_next) {
-      st.issue(Qg, q0 + BQ, N, aQ + (buf ^ 1) * kTileBytes);
-      st.issue(Gg, q0 + BQ, N, aG + (buf ^ 1) * kTileBytes);
+      st.issue(Qg, q0 + BQ, Nq, aQ + (buf ^ 1) * kTileBytes);
+      st.issue(Gg, q0 + BQ, Nq, aG + (buf ^ 1) * kTileBytes);
       load_rows(i + 1);
     }
-    dkdv_block<D, CAUSAL, MASK>(sQ[buf], sG[buf], sL[buf], sD[buf], q0, N, key, lane, a.sl2, f, dk, dv);
+    dkdv_block<D, CAUSAL, MASK>(sQ[buf], sG[buf], sL[buf], sD[buf], q0, Nq, a.coff, key, lane, a.sl2, f, dk, dv);
     if (has_next) store_rows(buf ^ 1);
     wait_vm0();
     __syncthreads();
@@ -509,21 +517,23 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   using plain = std::integral_constant<bool, false>;
 
   if (i < n_q) {
-    st.issue(Qg, i * BQ, N, aQ);
-    st.issue(Gg, i * BQ, N, aG);
+    st.issue(Qg, i * BQ, Nq, aQ);
+    st.issue(Gg, i * BQ, Nq, aG);
     load_rows(i);
     store_rows(0);
   }
   wait_vm0();
   __syncthreads();
-  const int n_full = N / BQ;  // blocks lying entirely inside the sequence
-  if (CAUSAL && i < n_q) step(masked{});
+  const int n_full = Nq / BQ;  // blocks lying entirely inside the sequence
+  // At most two leading masked blocks: their 127 query rows span at most two 128-row blocks.
+  if (CAUSAL && i < i_lead) step(masked{});
+  if (CAUSAL && i < i_lead) step(masked{});
   while (i < n_full) step(plain{});
   if (i < n_q) step(masked{});
 
-  if (key < N) {
-    uint16_t* dkr = a.dk + hoff + (int64_t)key * D;
-    uint16_t* dvr = a.dv + hoff + (int64_t)key * D;
+  if (key < Nk) {
+    uint16_t* dkr = a.dk + koff + (int64_t)key * D;
+    uint16_t* dvr = a.dv + koff + (int64_t)key * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -542,7 +552,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------------------------
 hipError_t launch_bwd_delta(BwdArgs a, int d, hipStream_t s) {
-  const int64_t total = (int64_t)a.BH * a.N;
+  const int64_t total = (int64_t)a.BH * a.Nq;
+  if (total == 0) return hipSuccess;
   const int rpb = kThreads / (d / 8);
   const int64_t grid = (total + rpb - 1) / rpb;
   if (d == 64)
@@ -553,7 +564,8 @@ hipError_t launch_bwd_delta(BwdArgs a, int d, hipStream_t s) {
 }
 
 hipError_t launch_bwd_dq(BwdArgs a, int d, bool causal, hipStream_t s) {
-  a.n_tiles = (a.N + kDqBr - 1) / kDqBr;
+  a.n_tiles = (a.Nq + kDqBr - 1) / kDqBr;
+  if (a.n_tiles == 0 || a.BH == 0) return hipSuccess;
   const dim3 grid(a.n_tiles * a.BH);
   if (d == 64) {
     if (causal) hipLaunchKernelGGL((dq_kernel<64, true>), grid, dim3(kThreads), 0, s, a);
@@ -566,7 +578,8 @@ hipError_t launch_bwd_dq(BwdArgs a, int d, bool causal, hipStream_t s) {
 }
 
 hipError_t launch_bwd_dkdv(BwdArgs a, int d, bool causal, hipStream_t s) {
-  a.n_tiles = (a.N + kDkvBk - 1) / kDkvBk;
+  a.n_tiles = (a.Nk + kDkvBk - 1) / kDkvBk;
+  if (a.n_tiles == 0 || a.BH == 0) return hipSuccess;
   const dim3 grid(a.n_tiles * a.BH);
   if (d == 64) {
     if (causal) hipLaunchKernelGGL((dkdv_kernel<64, true>), grid, dim3(kThreads), 0, s, a);

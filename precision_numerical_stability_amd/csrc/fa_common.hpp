@@ -256,6 +256,11 @@ __device__ __forceinline__ void sched_reads_ahead_valu() {
 // done: s_waitcnt vmcnt(0), other counters left at their maximum.
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Blocks of bc consecutive rows (from row 0) that hold any row of 0..last; 0 when last < 0.
+__device__ __forceinline__ int blocks_through(int last, int bc) { return last < 0 ? 0 : last / bc + 1; }
+// Blocks of bc consecutive rows (from row 0) that lie entirely within 0..last.
+__device__ __forceinline__ int blocks_within(int last, int bc) { return last < 0 ? 0 : (last + 1) / bc; }
+
 // Workgroup -> (head, tile rank).  The hardware hands consecutive workgroup ids to the 8 XCDs in
 // turn, so when the head count divides by 8, id x runs on XCD x % 8 and that XCD is given the
 // heads congruent to it: the concurrently running tiles of a head then share one XCD's L2.

@@ -68,30 +68,31 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   int bh, rank;
   map_block(blockIdx.x, a.BH, a.n_tiles, bh, rank);
   const int qt = CAUSAL ? a.n_tiles - 1 - rank : rank;
-  const int N = a.N;
+  const int Nq = a.Nq, Nk = a.Nk;
   const int q0 = qt * BR;
-  const int64_t hoff = (int64_t)bh * N * D;
-  const uint16_t* Qg = a.q + hoff;
-  const uint16_t* Kg = a.k + hoff;
-  const uint16_t* Vg = a.v + hoff;
+  const int64_t qoff = (int64_t)bh * Nq * D;
+  const int64_t koff = (int64_t)bh * Nk * D;
+  const uint16_t* Qg = a.q + qoff;
+  const uint16_t* Kg = a.k + koff;
+  const uint16_t* Vg = a.v + koff;
 
   const int qw0 = q0 + wave * 32;  // first query of this wave
-  const int qrow = qw0 + l32;      // this lane's query
+  const int qrow = qw0 + l32;      // this lane's query (causal: it sees keys up to qrow + coff)
 
   // Q^T as the B operand: lane holds Q[qrow][16 ks + 8 hh .. + 7].
   bf16x8 qf[KS];
   {
-    const uint16_t* src = Qg + (int64_t)min(qrow, N - 1) * D + 8 * hh;
+    const uint16_t* src = Qg + (int64_t)min(qrow, Nq - 1) * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const i32x4*>(src + 16 * ks));
   }
 
-  int n_kv = (N + BC - 1) / BC;
-  if (CAUSAL) n_kv = min(n_kv, (q0 + BR - 1) / BC + 1);
-  // Blocks this wave has anything visible in (causal: keys up to its last query).
-  const int n_mine = CAUSAL ? min(n_kv, (qw0 + 31) / BC + 1) : n_kv;
+  int n_kv = (Nk + BC - 1) / BC;
+  if (CAUSAL) n_kv = min(n_kv, blocks_through(q0 + BR - 1 + a.coff, BC));
+  // Blocks this wave has anything visible in (causal: keys up to its last query's limit).
+  const int n_mine = CAUSAL ? min(n_kv, blocks_through(qw0 + 31 + a.coff, BC)) : n_kv;
   // Leading blocks visible to every query of this wave need no mask.
-  const int n_plain = min(n_mine, CAUSAL ? qw0 / BC : N / BC);
+  const int n_plain = min(n_mine, CAUSAL ? min(blocks_within(qw0 + a.coff, BC), Nk / BC) : Nk / BC);
 
   f32x16 oacc[DT];
 #pragma unroll
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   stg.init(tid & (kFwdThreads / 2 - 1));
   constexpr uint32_t kTileBytes = BC * D * 2;
   const uint32_t aK = lds_addr(&sK[0][0]), aV = lds_addr(&sV[0][0]);
-  if (grp == 0) stg.issue(Kg, 0, N, aK);
+  if (grp == 0) stg.issue(Kg, 0, Nk, aK);
   // Everyone waits here: the Q fragments above are then known complete, so no wait for them is
   // left inside the loop (where the tile loads would make it wait for those as well).
   wait_vm0();
@@ -187,14 +188,17 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   // Vector phase V(j): online-softmax update for block j.
   auto vector_phase = [&](int j) __attribute__((always_inline)) {
     if (j >= n_mine) return;
-    const int kv0 = j * BC;
     if (j >= n_plain) {
+      // Key indices are taken relative to coff (all scalar arithmetic), so the causal test
+      // compares with the lane's query directly: key - coff > qrow.
+      const int kv0 = j * BC - a.coff;
+      const int nk = Nk - a.coff;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const bool hide = (key >= N) || (CAUSAL && key > qrow);
+          const bool hide = (key >= nk) || (CAUSAL && key > qrow);
           s[kb][r] = hide ? -INFINITY : s[kb][r];
         }
     }
@@ -307,10 +311,10 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   // for both at the end of its V(j), before K_{j+1} and V_j are read in phase 2j+2.
   auto iteration = [&](int j, auto par_tag) __attribute__((always_inline)) {
     constexpr int PAR = decltype(par_tag)::value;
-    if (grp == 0 && j + 1 < n_kv) stg.issue(Kg, (j + 1) * BC, N, aK + (PAR ^ 1) * kTileBytes);
+    if (grp == 0 && j + 1 < n_kv) stg.issue(Kg, (j + 1) * BC, Nk, aK + (PAR ^ 1) * kTileBytes);
     matrix_phase(j, par_tag);
     __syncthreads();
-    if (grp == 0 && j < n_kv) stg.issue(Vg, j * BC, N, aV + PAR * kTileBytes);
+    if (grp == 0 && j < n_kv) stg.issue(Vg, j * BC, Nk, aV + PAR * kTileBytes);
     vector_phase(j);
     if (grp == 0) wait_vm0();
     __syncthreads();
@@ -330,27 +334,34 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   const float ltot = KAHAN ? halves_sum(rs.lsum - rs.lcomp) : halves_sum(rs.lsum);
   const float row_min = STATS ? halves_min(rs.run_min) : 0.f;
   const int ones_tot = STATS ? halves_sum_i(rs.n_ones) : 0;
-  if (qrow < N) {
-    const float inv = 1.f / ltot;
-    uint16_t* orow = a.o + hoff + (int64_t)qrow * D;
+  if (qrow < Nq) {
+    // A query that sees no key (no keys at all, or bottom-right alignment with more queries than
+    // keys) has the empty sum: O = 0 and LSE = -inf.  Its lanes ran with an infinite max, so their
+    // accumulators are not used.
+    const bool empty = (Nk == 0) || (CAUSAL && qrow + a.coff < 0);
+    const float inv = empty ? 0.f : 1.f / ltot;
+    uint16_t* orow = a.o + qoff + (int64_t)qrow * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int d0 = 32 * dt + 8 * rr + 4 * hh;
+        float x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[u] = empty ? 0.f : oacc[dt][4 * rr + u] * inv;
         i32x2 w;
-        w[0] = (int)pack_bf16x2(oacc[dt][4 * rr] * inv, oacc[dt][4 * rr + 1] * inv);
-        w[1] = (int)pack_bf16x2(oacc[dt][4 * rr + 2] * inv, oacc[dt][4 * rr + 3] * inv);
+        w[0] = (int)pack_bf16x2(x[0], x[1]);
+        w[1] = (int)pack_bf16x2(x[2], x[3]);
         *reinterpret_cast<i32x2*>(orow + d0) = w;
       }
     if (hh == 0) {
-      const int64_t ri = (int64_t)bh * N + qrow;
-      a.lse[ri] = (rs.m2 + __log2f(ltot)) * kLn2;
+      const int64_t ri = (int64_t)bh * Nq + qrow;
+      a.lse[ri] = empty ? -INFINITY : (rs.m2 + __log2f(ltot)) * kLn2;
       if (STATS) {
-        if (a.dupcnt) a.dupcnt[ri] = rs.run_cnt;
-        if (a.ones) a.ones[ri] = ones_tot;
-        if (a.smin) a.smin[ri] = row_min * a.scale;
-        if (a.smax) a.smax[ri] = rs.run_max * a.scale;
+        if (a.dupcnt) a.dupcnt[ri] = empty ? 0 : rs.run_cnt;
+        if (a.ones) a.ones[ri] = empty ? 0 : ones_tot;
+        if (a.smin) a.smin[ri] = empty ? INFINITY : row_min * a.scale;
+        if (a.smax) a.smax[ri] = empty ? -INFINITY : rs.run_max * a.scale;
       }
     }
   }
@@ -383,7 +394,8 @@ int fwd_kv_block(int d, bool causal) {
 int fwd_q_block(int d) { return (d == 64 || d == 128) ? kFwdBr : 0; }
 
 hipError_t launch_fwd(FwdArgs a, int d, bool causal, int mode, bool stats, bool kahan, hipStream_t s) {
-  a.n_tiles = (a.N + kFwdBr - 1) / kFwdBr;
+  a.n_tiles = (a.Nq + kFwdBr - 1) / kFwdBr;
+  if (a.n_tiles == 0 || a.BH == 0) return hipSuccess;
   if (d == 64)
     return causal ? launch_fwd_mode<64, true>(a, mode, stats, kahan, s)
                   : launch_fwd_mode<64, false>(a, mode, stats, kahan, s);

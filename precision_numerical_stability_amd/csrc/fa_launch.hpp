@@ -18,7 +18,9 @@ struct FwdArgs {
   float* smin;      // may be null: per-row min of the scaled visible scores
   float* smax;      // may be null: per-row max of the scaled visible scores
   int BH;           // B * H
-  int N;
+  int Nq;           // queries per head
+  int Nk;           // keys per head
+  int coff;         // causal: key j is visible to query i iff j <= i + coff
   int n_tiles;      // query tiles per head (set by launch_fwd)
   float sl2;        // scale * log2(e)
   float scale;
@@ -37,7 +39,9 @@ struct BwdArgs {
   uint16_t* dv;
   float* delta;
   int BH;
-  int N;
+  int Nq;       // queries per head
+  int Nk;       // keys per head
+  int coff;     // causal: key j is visible to query i iff j <= i + coff
   int n_tiles;  // set by each launcher
   float scale;
   float sl2;    // scale * log2(e)

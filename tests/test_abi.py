@@ -157,3 +157,44 @@ def test_fwd_stats_rejects_bad_arguments(lib):
     assert call(q=None) == 1  # FA_ERR_NULL
     assert call(smin=ctypes.c_void_p(0x7F0000000002)) == 5  # FA_ERR_ALIGN
     assert call(smax=ctypes.c_void_p(0x7F0000000001)) == 5
+
+
+def _fwd_qk(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=2, Nq=128, Nk=64, d=64, causal=2, flags=0):
+    return lib.fa_fwd_qk(q, k, v, o, lse, None, None, None, None, B, H, Nq, Nk, d, causal, 0.125, 1.25,
+                         1, flags, None)
+
+
+def _bwd_qk(lib, ptrs=None, B=1, H=2, Nq=128, Nk=64, d=64, causal=2, stages=7):
+    p = list(ptrs or [P] * 10)
+    return lib.fa_bwd_qk(*p, B, H, Nq, Nk, d, causal, 0.125, 1.25, 1, stages, None)
+
+
+def test_qk_entry_points_validate(lib, ffi):
+    for causal in (-1, 3):
+        assert _fwd_qk(lib, causal=causal) == ffi.FA_ERR_PARAM
+        assert _bwd_qk(lib, causal=causal) == ffi.FA_ERR_PARAM
+    assert _fwd_qk(lib, Nk=-1) == ffi.FA_ERR_SHAPE and _bwd_qk(lib, Nq=-1) == ffi.FA_ERR_SHAPE
+    assert _fwd_qk(lib, Nk=1 << 23, d=128) == ffi.FA_ERR_SHAPE  # one head's keys over 2 GiB
+    assert _fwd_qk(lib, flags=4) == ffi.FA_ERR_PARAM
+    assert _fwd_qk(lib, k=None) == ffi.FA_ERR_NULL and _fwd_qk(lib, lse=None) == ffi.FA_ERR_NULL
+    assert _fwd_qk(lib, v=MIS) == ffi.FA_ERR_ALIGN
+    # k and v may be NULL when there are no keys; nothing runs when there are no queries
+    assert _fwd_qk(lib, q=None, k=None, v=None, o=None, lse=None, Nq=0) == ffi.FA_OK
+    assert _fwd_qk(lib, B=0, q=None) == ffi.FA_OK
+    for i in range(10):
+        ptrs = [P] * 10
+        ptrs[i] = None
+        assert _bwd_qk(lib, ptrs) == ffi.FA_ERR_NULL, i
+    assert _bwd_qk(lib, [None] * 10, Nq=0, Nk=0) == ffi.FA_OK
+    assert _bwd_qk(lib, stages=0) == ffi.FA_ERR_PARAM
+    # the square entry points keep accepting only causal 0 or 1
+    assert lib.fa_fwd(P, P, P, P, P, 1, 2, 128, 64, 2, 0.125, 1.25, 1, None) == ffi.FA_ERR_PARAM
+    assert _bwd(lib, causal=2) == ffi.FA_ERR_PARAM
+
+
+@pytest.mark.skipif(_gpu_present(), reason="needs a host without a GPU (fake pointers would be launched)")
+def test_qk_without_a_device_reports_hip_error(lib, ffi):
+    # Nq == 0: the forward is a no-op, the backward still has dK/dV to clear (a launch)
+    assert _fwd_qk(lib, Nq=0) == ffi.FA_OK
+    assert _bwd_qk(lib, Nq=0) == ffi.FA_ERR_HIP
+    assert _fwd_qk(lib, Nk=0, k=None, v=None) == ffi.FA_ERR_HIP

@@ -50,3 +50,16 @@ def test_config_table():
     assert CONFIGS[4].causal and abs(CONFIGS[4].scale - 128 ** -0.5) < 1e-8
     assert CONFIGS[5].N == 16384 and CONFIGS[5].kind == "grid"
     assert not CONFIGS[1].causal and CONFIGS[1].scale == 0.125
+
+
+def test_rect_inputs_shapes_and_determinism():
+    from inputs import rect_inputs
+    a = rect_inputs(2, 3, 70, 300, 64, seed=5)
+    b = rect_inputs(2, 3, 70, 300, 64, seed=5)
+    assert a["q"].shape == (2, 3, 70, 64) and a["do"].shape == (2, 3, 70, 64)
+    assert a["k"].shape == (2, 3, 300, 64) and a["v"].shape == (2, 3, 300, 64)
+    for name in a:
+        assert torch.equal(a[name], b[name]) and a[name].dtype == torch.bfloat16
+    g = rect_inputs(1, 1, 8, 16, 128, seed=5, grid=True)
+    vals = set(g["q"].float().unique().tolist()) | set(g["k"].float().unique().tolist())
+    assert vals <= set(GRID_VALUES)

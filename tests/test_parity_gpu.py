@@ -372,3 +372,137 @@ def test_empty_problem(fa):
     q = torch.empty((0, 2, 128, 64), dtype=torch.bfloat16, device=DEV)
     o, lse = fa.forward(q, q, q, True, 0.125)
     assert o.numel() == 0 and lse.numel() == 0
+
+
+# ---------------------------------------------------------------------------------------------
+# Nq != Nk, and the bottom-right causal alignment (fa_fwd_qk / fa_bwd_qk)
+
+from inputs import rect_inputs  # noqa: E402
+
+
+def run_rect(fa, t, causal, scale, mode, monitor=False):
+    g = _to_dev(t)
+    out = fa.forward(g["q"], g["k"], g["v"], causal, scale, BETA, mode, stats=True, monitor=monitor)
+    o, lse, dup, ones = out[:4]
+    dq, dk, dv = fa.backward(g["q"], g["k"], g["v"], o, lse, g["do"], causal, scale)
+    torch.cuda.synchronize()
+    res = {"o": o, "lse": lse, "dup": dup, "ones": ones, "dq": dq, "dk": dk, "dv": dv}
+    if monitor:
+        res.update(smin=out[4], smax=out[5])
+    res = {k_: (v_.float() if v_.dtype == torch.bfloat16 else v_).cpu().numpy() for k_, v_ in res.items()}
+    for k_ in ("o", "dq", "dk", "dv", "dup", "ones"):
+        assert np.all(np.isfinite(res[k_])), f"non-finite values in {k_}"
+    return res
+
+
+def check_rect_head(res, t, b, h, causal, scale, mode, counts_exact=False, bc=None):
+    x = _np64(t, b, h)
+    fr = oracle.forward(x["q"], x["k"], x["v"], causal, scale, BETA, mode)
+    check_o(res["o"][b, h], fr.o, f"O[{b},{h}]")
+    lse = res["lse"][b, h]
+    empty = fr.lse == -np.inf
+    assert np.array_equal(lse == -np.inf, empty), "rows with LSE = -inf differ"
+    assert np.all(np.isfinite(lse[~empty]))
+    if (~empty).any():
+        check_lse(lse[~empty], fr.lse[~empty])
+    assert np.all(res["o"][b, h][empty] == 0) and np.all(res["dup"][b, h][empty] == 0)
+    assert np.all(res["ones"][b, h][empty] == 0)
+    if counts_exact:
+        assert np.array_equal(res["dup"][b, h], fr.rs), f"dupcnt[{b},{h}] differs"
+        want = oracle.tiled_ones(x["q"], x["k"], causal, scale, BETA, mode, bc=bc)
+        assert np.array_equal(res["ones"][b, h], want), f"ones[{b},{h}] differs"
+    br = oracle.backward(x["q"], x["k"], x["v"], x["do"], causal, scale, o=fr.o, lse=fr.lse)
+    for name, ref in (("dq", br.dq), ("dk", br.dk), ("dv", br.dv)):
+        check_grad(res[name][b, h], ref, f"{name}[{b},{h}]")
+    assert np.all(res["dq"][b, h][empty] == 0)
+    return fr
+
+
+RECT_SHAPES = [(37, 300), (300, 37), (128, 200), (200, 128), (1, 333), (333, 1), (256, 513), (513, 256)]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [0, 1, 2])
+@pytest.mark.parametrize("nq,nk", RECT_SHAPES)
+def test_rectangular_parity(fa, d, causal, nq, nk):
+    _say("rect", d, causal, nq, nk)
+    t = rect_inputs(2, 2, nq, nk, d, seed=900 + nq + 3 * nk + d + causal)
+    scale = d ** -0.5
+    res = run_rect(fa, t, causal, scale, 1)
+    for b, h in ((0, 0), (1, 1)):
+        check_rect_head(res, t, b, h, causal, scale, 1)
+
+
+@pytest.mark.parametrize("causal", [0, 1, 2])
+@pytest.mark.parametrize("nq,nk", [(96, 416), (416, 96), (320, 300)])
+def test_rectangular_grid_counts(fa, causal, nq, nk):
+    """Grid inputs (exact fp32 dot products): repeat counts and exact-1.0 counts bit-exact in
+    every mode, with the key-block replay of the oracle."""
+    _say("rect-grid", causal, nq, nk)
+    t = rect_inputs(1, 2, nq, nk, 128, seed=77 + nq + nk + causal, grid=True)
+    scale = 128 ** -0.5
+    for mode in (0, 1, 2):
+        res = run_rect(fa, t, causal, scale, mode)
+        for h in range(2):
+            check_rect_head(res, t, 0, h, causal, scale, mode, counts_exact=True,
+                            bc=fa.fa_fwd_kv_block(128, causal))
+
+
+def test_rectangular_monitors_on_empty_rows(fa):
+    _say("rect-monitor")
+    t = rect_inputs(1, 2, 300, 100, 64, seed=31)
+    scale = 0.125
+    res = run_rect(fa, t, 2, scale, 2, monitor=True)
+    for h in range(2):
+        x = _np64(t, 0, h)
+        fr = oracle.forward(x["q"], x["k"], x["v"], 2, scale, BETA, 2)
+        empty = fr.lse == -np.inf
+        assert empty.sum() == 200
+        assert np.all(res["smin"][0, h][empty] == np.inf) and np.all(res["smax"][0, h][empty] == -np.inf)
+        np.testing.assert_allclose(res["smin"][0, h][~empty], fr.smin[~empty], rtol=1e-5, atol=1e-5)
+        np.testing.assert_allclose(res["smax"][0, h][~empty], fr.rm[~empty], rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("causal", [0, 1, 2])
+def test_square_alignments_agree(fa, causal):
+    """Nq == Nk: fa_fwd_qk / fa_bwd_qk equal the square entry points bit for bit, and the two
+    causal alignments coincide."""
+    _say("square-qk", causal)
+    g = _to_dev(make_inputs(2, B=1, H=4, N=384))
+    sq = 1 if causal else 0
+    o1, lse1 = torch.empty_like(g["q"]), torch.empty(g["q"].shape[:3], dtype=torch.float32, device=DEV)
+    fa.fa_fwd(g["q"], g["k"], g["v"], o1, lse1, sq, 0.125, BETA, 1)
+    o2, lse2 = fa.forward(g["q"], g["k"], g["v"], causal, 0.125, BETA, 1)
+    grads = []
+    for c, o, lse in ((sq, o1, lse1), (causal, o2, lse2)):
+        dq, dk, dv = (torch.empty_like(g["q"]) for _ in range(3))
+        delta = torch.empty_like(lse)
+        if c == sq:
+            fa.fa_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], dq, dk, dv, delta, c, 0.125)
+        else:
+            fa.fa_bwd_qk(g["q"], g["k"], g["v"], o, lse, g["do"], dq, dk, dv, delta, c, 0.125)
+        grads.append((dq, dk, dv))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(lse1, lse2)
+    for a, b in zip(*grads):
+        assert torch.equal(a, b)
+
+
+def test_no_keys_and_no_queries(fa):
+    _say("rect-empty")
+    q = torch.randn((1, 2, 70, 64), device=DEV).to(torch.bfloat16)
+    kv0 = torch.empty((1, 2, 0, 64), dtype=torch.bfloat16, device=DEV)
+    for causal in (0, 1, 2):
+        o, lse = fa.forward(q, kv0, kv0, causal, 0.125)
+        dq, dk, dv = fa.backward(q, kv0, kv0, o, lse, q, causal, 0.125)
+        torch.cuda.synchronize()
+        assert torch.all(o == 0) and torch.all(lse == -float("inf")) and torch.all(dq == 0)
+        assert dk.numel() == 0 and dv.numel() == 0
+    k = torch.randn((1, 2, 90, 64), device=DEV).to(torch.bfloat16)
+    q0 = torch.empty((1, 2, 0, 64), dtype=torch.bfloat16, device=DEV)
+    o, lse = fa.forward(q0, k, k, 2, 0.125)
+    dk = torch.full_like(k, 7.0)
+    dv = torch.full_like(k, 7.0)
+    fa.fa_bwd_qk(q0, k, k, o, lse, q0, q0.clone(), dk, dv, torch.empty((1, 2, 0), device=DEV), 2, 0.125)
+    torch.cuda.synchronize()
+    assert torch.all(dk == 0) and torch.all(dv == 0)
