@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE: imported only by the test suite, the package smoke check and the
 CPU-baseline leg of the benchmark.  It shares no code with the HIP library and never imports it.
 """
-from .attention import (MODE_STANDARD, MODE_TIE_RULE, MODE_TIE_ANTICIPATE, bf16_round, visible,
+from .attention import (MODE_STANDARD, MODE_TIE_RULE, MODE_TIE_ANTICIPATE, bf16_round, fp16_round, visible,
                         scaled_scores, row_max_and_repeats, stable_shift, forward, forward_rows,
                         backward, dq_rows,
                         probabilities, forward_bhnd, backward_bhnd, flops_forward,
@@ -12,7 +12,7 @@ from .attention import (MODE_STANDARD, MODE_TIE_RULE, MODE_TIE_ANTICIPATE, bf16_
 from .tiled import tiled_forward, tiled_ones
 
 __all__ = [
-    "MODE_STANDARD", "MODE_TIE_RULE", "MODE_TIE_ANTICIPATE", "bf16_round", "visible",
+    "MODE_STANDARD", "MODE_TIE_RULE", "MODE_TIE_ANTICIPATE", "bf16_round", "fp16_round", "visible",
     "scaled_scores", "row_max_and_repeats", "stable_shift", "forward", "forward_rows",
     "backward", "dq_rows",
     "probabilities", "forward_bhnd", "backward_bhnd", "flops_forward", "exact_causal_pairs",

@@ -79,6 +79,24 @@ def visible(rows, n_keys, causal, n_queries=None):
     return keys[None, :] <= rows[:, None] + off
 
 
+def fp16_round(x):
+    """Round float64 values to the nearest IEEE binary16 value, ties to even, as float64.
+
+    binary16 keeps 11 significant bits for normal values (|x| >= 2^-14) and a fixed spacing of
+    2^-24 below that (subnormals, the 5.96e-8 lower end of the range [FA-practice] §2.1 gives);
+    values that round above the largest finite value 65504 become +-inf ([FA-backward] §3.1:
+    e^12 overflows, e^11 does not).  Rounded directly from fp64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, expo = np.frexp(x)  # x = mant * 2**expo, |mant| in [0.5, 1)
+    e = np.maximum(expo, -13)  # below 2^-14 the spacing stays 2^-24 = 2^(-13 - 11)
+    r = np.ldexp(np.rint(np.ldexp(x, 11 - e)), e - 11)
+    return np.where(np.abs(r) > 65504.0, np.copysign(np.inf, x), r)
+
+
+ELEM_ROUND = {"bf16": bf16_round, "f16": fp16_round}
+
+
 def scaled_scores(q_rows, k, scale, mask):
     """S = scale * q k^T for a block of query rows; invisible entries are -inf.
 
@@ -130,15 +148,18 @@ class ForwardResult:
     rs: np.ndarray  # [N] number of visible keys attaining the row max (int64)
     m: np.ndarray  # [N] the row shift actually used
     l: np.ndarray  # [N] sum of the unnormalised probabilities exp(S - m)
-    ones: np.ndarray  # [N] count of bf16(exp(S - m)) == 1.0 over visible keys (int64)
+    ones: np.ndarray  # [N] count of round(exp(S - m)) == 1.0 over visible keys (int64), rounded
+    #                  to the 16-bit element type of the P^ V product
     smin: np.ndarray  # [N] row min of the scaled scores over visible keys
 
 
-def forward_rows(q, k, v, rows, causal, scale, beta=1.25, mode=MODE_STANDARD):
+def forward_rows(q, k, v, rows, causal, scale, beta=1.25, mode=MODE_STANDARD, elem="bf16"):
     """The forward of one head for the query rows `rows` (absolute indices into q; the causal mask
     uses them), evaluated without tiling: P_hat = exp(S - m), l = rowsum(P_hat),
     O = diag(l)^-1 P_hat V and LSE = m + ln l ([BF16-FA] §2.1, [FA-practice] §3.3,
-    [FA-backward] §2).  Returns a ForwardResult whose arrays are indexed like `rows`."""
+    [FA-backward] §2).  `elem` ("bf16" or "f16") is the 16-bit type P^ is rounded to for the
+    P^ V product ([FA-practice] §3.2 names both); it only affects the exact-1.0 count.  Returns a
+    ForwardResult whose arrays are indexed like `rows`."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -155,14 +176,14 @@ def forward_rows(q, k, v, rows, causal, scale, beta=1.25, mode=MODE_STANDARD):
     with np.errstate(divide="ignore", invalid="ignore"):
         o = np.where(live[:, None], (p_hat @ v) / l[:, None], 0.0)
         lse = np.where(live, m + np.log(l), -np.inf)
-    ones = np.sum((bf16_round(p_hat) == 1.0) & mask, axis=1)
+    ones = np.sum((ELEM_ROUND[elem](p_hat) == 1.0) & mask, axis=1)
     # The range of the softmax input, to be monitored ([FA-practice] §5): min over visible keys
     # (+inf for a row with none, the min of the empty set).
     smin = np.min(np.where(mask, s, np.inf), axis=1, initial=np.inf)
     return ForwardResult(o, lse, rm, rs, m, l, ones, smin)
 
 
-def forward(q, k, v, causal, scale, beta=1.25, mode=MODE_STANDARD, row_chunk=1024):
+def forward(q, k, v, causal, scale, beta=1.25, mode=MODE_STANDARD, row_chunk=1024, elem="bf16"):
     """One head of attention: q [Nq, d], k [Nk, d], v [Nk, d] (float64): forward_rows over all
     rows, in chunks of row_chunk rows to bound memory."""
     q = np.asarray(q, dtype=np.float64)
@@ -179,7 +200,7 @@ def forward(q, k, v, causal, scale, beta=1.25, mode=MODE_STANDARD, row_chunk=102
     smin = np.zeros(n)
     for r0 in range(0, n, row_chunk):
         rows = np.arange(r0, min(n, r0 + row_chunk))
-        fr = forward_rows(q, k, v, rows, causal, scale, beta, mode)
+        fr = forward_rows(q, k, v, rows, causal, scale, beta, mode, elem)
         o[rows], lse[rows] = fr.o, fr.lse
         rm_all[rows], rs_all[rows], m_all[rows], l_all[rows], ones[rows] = fr.rm, fr.rs, fr.m, fr.l, fr.ones
         smin[rows] = fr.smin
@@ -264,7 +285,8 @@ def _heads(x):
     return x
 
 
-def forward_bhnd(q, k, v, causal, scale, beta=1.25, mode=MODE_STANDARD, heads=None, row_chunk=1024):
+def forward_bhnd(q, k, v, causal, scale, beta=1.25, mode=MODE_STANDARD, heads=None, row_chunk=1024,
+                 elem="bf16"):
     """forward() over [B, H, N, d] arrays.  `heads` restricts the work to a list of (b, h) pairs;
     the other entries of the outputs stay zero.  Returns a dict of stacked arrays."""
     q, k, v = _heads(q), _heads(k), _heads(v)
@@ -281,7 +303,7 @@ def forward_bhnd(q, k, v, causal, scale, beta=1.25, mode=MODE_STANDARD, heads=No
     }
     pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
     for b, h in pairs:
-        fr = forward(q[b, h], k[b, h], v[b, h], causal, scale, beta, mode, row_chunk)
+        fr = forward(q[b, h], k[b, h], v[b, h], causal, scale, beta, mode, row_chunk, elem)
         for name in out:
             out[name][b, h] = getattr(fr, name)
     return out

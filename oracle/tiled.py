@@ -25,14 +25,15 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import bf16_round, stable_shift, visible
+from .attention import ELEM_ROUND, stable_shift, visible
 
 
-def tiled_forward(q, k, v, causal, scale, beta=1.25, mode=0, bc=64, order=None):
+def tiled_forward(q, k, v, causal, scale, beta=1.25, mode=0, bc=64, order=None, elem="bf16"):
     """Tiled forward over one head; returns dict(o, lse, r, c, m, ones).
 
     `order` lists the key-block indices in processing order (default: ascending).  Key blocks
-    entirely invisible to a row leave that row's state unchanged.
+    entirely invisible to a row leave that row's state unchanged.  `elem` ("bf16" or "f16") is the
+    type P^ is rounded to for the exact-1.0 count.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -66,7 +67,7 @@ def tiled_forward(q, k, v, causal, scale, beta=1.25, mode=0, bc=64, order=None):
         p_hat = np.where(mask, np.exp(s - np.where(live, m_new, 0.0)[:, None]), 0.0)
         l = alpha * l + p_hat.sum(axis=1)
         acc = alpha[:, None] * acc + p_hat @ v[k0:k1]
-        ones += np.sum((bf16_round(p_hat) == 1.0) & mask, axis=1)
+        ones += np.sum((ELEM_ROUND[elem](p_hat) == 1.0) & mask, axis=1)
         m = m_new
     # A row with no visible key keeps l = 0: O = 0 and LSE = -inf.
     with np.errstate(divide="ignore", invalid="ignore"):
@@ -75,7 +76,7 @@ def tiled_forward(q, k, v, causal, scale, beta=1.25, mode=0, bc=64, order=None):
     return {"o": o, "lse": lse, "r": r, "c": c, "m": m, "ones": ones}
 
 
-def tiled_ones(q, k, causal, scale, beta=1.25, mode=0, bc=64, order=None):
+def tiled_ones(q, k, causal, scale, beta=1.25, mode=0, bc=64, order=None, elem="bf16"):
     """Per-row count of exact-1.0 bf16 unnormalised probabilities under block-wise processing.
 
     Same recurrence as tiled_forward without V; used where only the count is needed (large
@@ -104,5 +105,5 @@ def tiled_ones(q, k, causal, scale, beta=1.25, mode=0, bc=64, order=None):
         live = np.isfinite(r)
         m = stable_shift(np.where(live, r, 0.0), c, beta, mode)
         p_hat = np.where(mask, np.exp(s - m[:, None]), 0.0)
-        ones += np.sum((bf16_round(p_hat) == 1.0) & mask, axis=1)
+        ones += np.sum((ELEM_ROUND[elem](p_hat) == 1.0) & mask, axis=1)
     return ones

@@ -63,6 +63,60 @@ def test_bf16_round_threshold_below_one():
     assert oracle.bf16_round(np.nextafter(1 - 2 ** -9, 0)) == 1 - 2 ** -8
 
 
+def test_fp16_round_matches_numpy_and_torch():
+    rng = np.random.default_rng(8)
+    x = np.concatenate([
+        rng.standard_normal(20000) * 300.0,
+        rng.uniform(0.998, 1.002, 20000),
+        np.exp(-rng.uniform(0, 20, 20000)),  # down through the subnormal range
+        np.exp(rng.uniform(10, 11.2, 2000)),  # up to and past the overflow threshold
+        -np.exp(rng.uniform(10, 11.2, 2000)),
+    ])
+    # exact ties: halfway between neighbours, including the subnormal and overflow boundaries
+    ties = np.array([1 + 2 ** -11, 1 + 3 * 2 ** -11, 1 - 2 ** -12, 2 ** -25, 3 * 2 ** -25,
+                     65520.0, 65488.0, -65520.0, 2 ** -14 + 2 ** -25])
+    x = np.concatenate([x, ties])
+    got = oracle.fp16_round(x)
+    ref = x.astype(np.float16).astype(np.float64)  # numpy rounds float64 -> binary16 directly
+    assert np.array_equal(got, ref, equal_nan=False)
+    x32 = x.astype(np.float32)  # torch's cast from values exact in fp32 (no double rounding)
+    ref32 = torch.from_numpy(x32).to(torch.float16).to(torch.float64).numpy()
+    assert np.array_equal(oracle.fp16_round(x32.astype(np.float64)), ref32)
+
+
+def test_fp16_round_pages_range():
+    g = json.load(open(os.path.join(GOLDEN, "pages_numbers.json")))
+    assert oracle.fp16_round(g["fp16_max"]["value"]) == 65504.0
+    assert oracle.fp16_round(65519.99) == 65504.0 and oracle.fp16_round(65520.0) == np.inf
+    assert oracle.fp16_round(math.exp(11)) == 59872.0  # e^11 survives (to the nearest 32)
+    assert oracle.fp16_round(math.exp(12)) == np.inf  # e^12 overflows
+    assert oracle.fp16_round(g["fp16_min_positive"]["value"]) == 2.0 ** -24
+    assert oracle.fp16_round(2.0 ** -25) == 0.0 and oracle.fp16_round(1.5 * 2 ** -25) == 2.0 ** -24
+    lo, hi = ONE_WINDOW["f16"]
+    assert oracle.fp16_round(lo) == 1.0 and oracle.fp16_round(np.nextafter(lo, 0)) < 1.0
+    assert oracle.fp16_round(hi) == 1.0 and oracle.fp16_round(np.nextafter(hi, 2)) > 1.0
+    lo, hi = ONE_WINDOW["bf16"]
+    assert oracle.bf16_round(lo) == 1.0 and oracle.bf16_round(hi) == 1.0
+    assert oracle.bf16_round(np.nextafter(hi, 2)) > 1.0
+
+
+def test_shifted_fp16_softmax_never_overflows():
+    """A softmax whose exponentials are rounded to fp16 overflows for scores above ln 65504 ~ 11.09
+    unless the row maximum (or the stabilised shift) is subtracted first: every shifted
+    unnormalised probability is at most 1 in every mode ([FA-backward] §3.1, §3.2)."""
+    rng = np.random.default_rng(12)
+    q, k, v = rng.standard_normal((64, 16)) * 2.0, rng.standard_normal((64, 16)) * 2.0, rng.standard_normal((64, 16))
+    scale = 0.6
+    s = scale * q @ k.T
+    assert s.max() > 12.0
+    assert np.isinf(oracle.fp16_round(np.exp(s))).any()
+    for mode in (0, 1, 2):
+        fr = oracle.forward(q, k, v, False, scale, BETA, mode, elem="f16")
+        p_hat = np.exp(s - fr.m[:, None])
+        assert p_hat.max() <= 1.0 + 1e-12 and np.all(np.isfinite(oracle.fp16_round(p_hat)))
+        assert np.all(np.isfinite(fr.o)) and np.all(np.isfinite(fr.lse))
+
+
 def test_pages_printed_numbers():
     g = json.load(open(os.path.join(GOLDEN, "pages_numbers.json")))
     assert np.float16(g["fp16_max"]["value"]) == np.finfo(np.float16).max
@@ -334,7 +388,13 @@ def test_gradient_invariants(causal):
 # P11: tile replay of the exact-1.0 count vs a scalar per-tile replay
 
 
-def _scalar_tile_ones(q, k, causal, scale, beta, mode, bc):
+# The interval of real values each 16-bit type rounds (RNE) to exactly 1.0, from the formats:
+# bf16 spacing is 2^-8 below 1 and 2^-7 above, fp16 2^-11 below and 2^-10 above.  Both midpoints
+# are ties, and 1.0 is the neighbour with the even last mantissa bit, so both round to 1.0.
+ONE_WINDOW = {"bf16": (1 - 2 ** -9, 1 + 2 ** -8), "f16": (1 - 2 ** -12, 1 + 2 ** -11)}
+
+
+def _scalar_tile_ones(q, k, causal, scale, beta, mode, bc, elem="bf16"):
     n = len(q)
     out = []
     for i in range(n):
@@ -351,21 +411,23 @@ def _scalar_tile_ones(q, k, causal, scale, beta, mode, bc):
             r = rn
             rep = c > 1 if mode == 1 else (mode == 2)
             m = beta * r if (r > 0 and rep) else (0.0 if (r < 0 and rep) else r)
+            lo, hi = ONE_WINDOW[elem]
             for x in s.values():
-                if oracle.bf16_round(math.exp(x - m)) == 1.0:
+                if lo <= math.exp(x - m) <= hi:
                     ones += 1
         out.append(ones)
     return np.array(out)
 
 
+@pytest.mark.parametrize("elem", ["bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("mode", [0, 1, 2])
-def test_tile_ones_vs_scalar_replay(causal, mode):
+def test_tile_ones_vs_scalar_replay(causal, mode, elem):
     t = _head(grid_inputs(1, 1, 48, 8, seed=17))
     scale = 0.35
-    want = _scalar_tile_ones(t["q"], t["k"], causal, scale, BETA, mode, 16)
-    got = oracle.tiled_ones(t["q"], t["k"], causal, scale, BETA, mode, bc=16)
-    got2 = oracle.tiled_forward(t["q"], t["k"], t["v"], causal, scale, BETA, mode, bc=16)["ones"]
+    want = _scalar_tile_ones(t["q"], t["k"], causal, scale, BETA, mode, 16, elem)
+    got = oracle.tiled_ones(t["q"], t["k"], causal, scale, BETA, mode, bc=16, elem=elem)
+    got2 = oracle.tiled_forward(t["q"], t["k"], t["v"], causal, scale, BETA, mode, bc=16, elem=elem)["ones"]
     assert np.array_equal(got, want)
     assert np.array_equal(got2, want)
 
