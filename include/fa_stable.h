@@ -1,6 +1,6 @@
 /*
- * fa_stable.h -- C ABI of a BF16 FlashAttention forward/backward library for AMD MI355X (gfx950),
- * with the stabilised safe-softmax shift for repeated row maxima.
+ * fa_stable.h -- C ABI of a BF16 (and FP16) FlashAttention forward/backward library for AMD
+ * MI355X (gfx950), with the stabilised safe-softmax shift for repeated row maxima.
  *
  * Operations (pages cited by title/address and section):
  *   - forward: the tiled online softmax of the BF16 Flash Attention article
@@ -18,6 +18,7 @@
  * Conventions shared by every entry point:
  *   - q, k, v, o, dO, dq, dk, dv: device pointers to contiguous [B, H, N, d] bfloat16 tensors
  *     (row-major, d fastest), 16-byte aligned.  bfloat16 is passed as raw 16-bit storage.
+ *     fa_fwd_elem / fa_bwd_elem also take IEEE binary16 (FA_ELEM_F16) in the same layout.
  *   - lse, delta workspace: device pointers to contiguous [B, H, N] float32, 4-byte aligned.
  *     lse holds the natural-log logsumexp of the scaled scores: LSE = m + ln(l).
  *   - dupcnt, ones: device pointers to contiguous [B, H, N] int32, 4-byte aligned.
@@ -59,7 +60,7 @@ typedef enum {
   FA_ERR_NULL = 1,    /* a required pointer is NULL */
   FA_ERR_SHAPE = 2,   /* B, H or a sequence length negative, or the problem too large */
   FA_ERR_HEADDIM = 3, /* d is not 64 or 128 */
-  FA_ERR_PARAM = 4,   /* causal, scale, beta or stable_flag out of range */
+  FA_ERR_PARAM = 4,   /* causal, scale, beta, stable_flag, flags, stages or elem out of range */
   FA_ERR_ALIGN = 5,   /* a pointer is not aligned as stated above */
   FA_ERR_HIP = 6      /* a HIP call failed; see fa_last_hip_error() */
 } fa_status;
@@ -158,6 +159,36 @@ int fa_bwd_qk(const void* q, const void* k, const void* v, const void* o, const 
               const void* dO, void* dq, void* dk, void* dv, float* delta_ws,
               int B, int H, int Nq, int Nk, int d, int causal, float scale, float beta,
               int stable_flag, int stages, void* stream);
+
+/* Element type of the 16-bit tensors (q, k, v, o, dO, dq, dk, dv) for fa_fwd_elem / fa_bwd_elem:
+ *   FA_ELEM_BF16 (0): bfloat16, the type every other entry point takes;
+ *   FA_ELEM_F16  (1): IEEE binary16.
+ * "Flash Attention低精度训练稳定性优化实践" (jsqmd.com/news/761560) §2.1 and §3.2 name both 16-bit
+ * formats for the attention inputs and the P V product: fp16 keeps 11 significant bits against
+ * bf16's 8 but tops out at 65504, so a score whose exponential exceeds it (e^12 ~ 1.63e5 already
+ * does, "FlashAttention 训练时为什么会梯度爆炸", cnnetsun.cn/a/2497354, §3.1) overflows unless the
+ * exponent is shifted first.  Every product still accumulates in fp32 and the softmax runs in fp32;
+ * with either element type the unnormalised probabilities P^ = exp(S - m) are at most 1 after the
+ * shift (P^ = 1 at a maximum only where m equals it), so they and P are in range, and they are
+ * rounded (to nearest even) to the element type for the P^ V, P^T dO and dS products.  The
+ * exact-1.0 count (ones) compares the element type's 1.0. */
+#define FA_ELEM_BF16 0
+#define FA_ELEM_F16 1
+
+/* fa_fwd_qk with the element type as an argument: fa_fwd_qk(...) ==
+ * fa_fwd_elem(..., flags, FA_ELEM_BF16, stream).  elem outside {0, 1} -> FA_ERR_PARAM. */
+int fa_fwd_elem(const void* q, const void* k, const void* v, void* o, float* lse,
+                int32_t* dupcnt, int32_t* ones, float* smin, float* smax,
+                int B, int H, int Nq, int Nk, int d, int causal, float scale, float beta,
+                int stable_flag, int flags, int elem, void* stream);
+
+/* fa_bwd_qk with the element type as an argument: fa_bwd_qk(...) ==
+ * fa_bwd_elem(..., stages, FA_ELEM_BF16, stream).  lse and delta_ws stay fp32.  elem outside
+ * {0, 1} -> FA_ERR_PARAM. */
+int fa_bwd_elem(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dO, void* dq, void* dk, void* dv, float* delta_ws,
+                int B, int H, int Nq, int Nk, int d, int causal, float scale, float beta,
+                int stable_flag, int stages, int elem, void* stream);
 
 /* Bytes of the delta workspace fa_bwd needs: B*H*N*4 (0 for invalid or empty shapes); for
  * fa_bwd_qk pass N = Nq. */

@@ -1,8 +1,8 @@
-"""Seeded bf16 input generators for the five attention workloads.
+"""Seeded 16-bit input generators for the five attention workloads.
 
 Every tensor is drawn on the CPU with a ``torch.Generator`` seeded per workload, as float32,
-multiplied by the workload's sigma, and rounded to bfloat16 by torch's round-to-nearest-even
-cast.  Q, K, V and dO are drawn in that order.  The workloads stand in for the attention layers
+multiplied by the workload's sigma, and rounded to bfloat16 (default) or float16 by torch's
+round-to-nearest-even cast.  Q, K, V and dO are drawn in that order.  The workloads stand in for the attention layers
 of the models the pages train (GPT-2 small/medium and LLaMA-7B shapes); no dataset or weight is
 involved.
 
@@ -18,7 +18,7 @@ import math
 import numpy as np
 import torch
 
-# Entries of the tie-heavy grid: exact in bf16, and every dot product of two rows of length
+# Entries of the tie-heavy grid: exact in bf16 and fp16, and every dot product of two rows of length
 # <= 512 drawn from it is an exact multiple of 0.25 in fp32.
 GRID_VALUES = (-1.0, -0.5, 0.0, 0.5, 1.0)
 
@@ -63,52 +63,55 @@ def _gen(seed: int) -> torch.Generator:
     return g
 
 
-def _randn_bf16(g: torch.Generator, shape, sigma: float = 1.0) -> torch.Tensor:
+def _randn16(g: torch.Generator, shape, sigma: float = 1.0, dtype=torch.bfloat16) -> torch.Tensor:
     x = torch.randn(shape, generator=g, dtype=torch.float32)
     if sigma != 1.0:
         x = x * sigma
-    return x.to(torch.bfloat16)
+    return x.to(dtype)
 
 
-def _grid_bf16(g: torch.Generator, shape) -> torch.Tensor:
+def _grid16(g: torch.Generator, shape, dtype=torch.bfloat16) -> torch.Tensor:
     idx = torch.randint(0, len(GRID_VALUES), shape, generator=g)
     table = torch.tensor(GRID_VALUES, dtype=torch.float32)
-    return table[idx].to(torch.bfloat16)
+    return table[idx].to(dtype)
 
 
-def randn_inputs(B, H, N, d, seed, sigma_qk=1.0):
-    """Q, K ~ N(0, sigma_qk^2), V, dO ~ N(0, 1); bf16, shape [B, H, N, d]."""
+def randn_inputs(B, H, N, d, seed, sigma_qk=1.0, dtype=torch.bfloat16):
+    """Q, K ~ N(0, sigma_qk^2), V, dO ~ N(0, 1); `dtype` (bf16 or fp16), shape [B, H, N, d]."""
     g = _gen(seed)
     shape = (B, H, N, d)
-    q = _randn_bf16(g, shape, sigma_qk)
-    k = _randn_bf16(g, shape, sigma_qk)
-    v = _randn_bf16(g, shape)
-    do = _randn_bf16(g, shape)
+    q = _randn16(g, shape, sigma_qk, dtype)
+    k = _randn16(g, shape, sigma_qk, dtype)
+    v = _randn16(g, shape, 1.0, dtype)
+    do = _randn16(g, shape, 1.0, dtype)
     return {"q": q, "k": k, "v": v, "do": do}
 
 
-def rect_inputs(B, H, Nq, Nk, d, seed, grid=False):
+def rect_inputs(B, H, Nq, Nk, d, seed, grid=False, dtype=torch.bfloat16):
     """Q and dO [B, H, Nq, d], K and V [B, H, Nk, d] for a query block attending to a key sequence
     of another length (drawn in the order Q, K, V, dO).  Q, K ~ N(0, 1), or uniform over
     GRID_VALUES with grid=True; V, dO ~ N(0, 1)."""
     g = _gen(seed)
     qs, ks = (B, H, Nq, d), (B, H, Nk, d)
-    draw = _grid_bf16 if grid else _randn_bf16
-    q = draw(g, qs)
-    k = draw(g, ks)
-    v = _randn_bf16(g, ks)
-    do = _randn_bf16(g, qs)
+    if grid:
+        q = _grid16(g, qs, dtype)
+        k = _grid16(g, ks, dtype)
+    else:
+        q = _randn16(g, qs, 1.0, dtype)
+        k = _randn16(g, ks, 1.0, dtype)
+    v = _randn16(g, ks, 1.0, dtype)
+    do = _randn16(g, qs, 1.0, dtype)
     return {"q": q, "k": k, "v": v, "do": do}
 
 
-def grid_inputs(B, H, N, d, seed):
+def grid_inputs(B, H, N, d, seed, dtype=torch.bfloat16):
     """Q, K uniform over GRID_VALUES (exact ties in row maxima are frequent); V, dO ~ N(0, 1)."""
     g = _gen(seed)
     shape = (B, H, N, d)
-    q = _grid_bf16(g, shape)
-    k = _grid_bf16(g, shape)
-    v = _randn_bf16(g, shape)
-    do = _randn_bf16(g, shape)
+    q = _grid16(g, shape, dtype)
+    k = _grid16(g, shape, dtype)
+    v = _randn16(g, shape, 1.0, dtype)
+    do = _randn16(g, shape, 1.0, dtype)
     return {"q": q, "k": k, "v": v, "do": do}
 
 
@@ -122,24 +125,26 @@ def _apply_dup(t):
 
 
 def _apply_sink(t):
-    """Key 0 of each (b, h) := bf16(4 * u), u = the mean query direction normalised to unit length."""
+    """Key 0 of each (b, h) := 4 * u rounded to the tensors' type, u = the mean query direction
+    normalised to unit length."""
     q, k = t["q"], t["k"]
     qm = q.to(torch.float64).mean(dim=2)  # [B, H, d]
     u = qm / qm.norm(dim=-1, keepdim=True).clamp_min(1e-30)
-    k[:, :, 0, :] = (4.0 * u).to(torch.bfloat16)
+    k[:, :, 0, :] = (4.0 * u).to(k.dtype)
     return t
 
 
-def make_inputs(cfg, **overrides):
-    """Inputs for a workload (a WorkloadConfig or its id); keyword overrides replace B/H/N/d/seed."""
+def make_inputs(cfg, dtype=torch.bfloat16, **overrides):
+    """Inputs for a workload (a WorkloadConfig or its id) in `dtype` (bf16 or fp16); keyword
+    overrides replace B/H/N/d/seed."""
     if not isinstance(cfg, WorkloadConfig):
         cfg = CONFIGS[int(cfg)]
     if overrides:
         cfg = cfg.with_shape(**overrides)
     if cfg.kind == "grid":
-        t = grid_inputs(cfg.B, cfg.H, cfg.N, cfg.d, cfg.seed)
+        t = grid_inputs(cfg.B, cfg.H, cfg.N, cfg.d, cfg.seed, dtype)
     else:
-        t = randn_inputs(cfg.B, cfg.H, cfg.N, cfg.d, cfg.seed, cfg.sigma_qk)
+        t = randn_inputs(cfg.B, cfg.H, cfg.N, cfg.d, cfg.seed, cfg.sigma_qk, dtype)
     if cfg.kind == "dup":
         t = _apply_dup(t)
     elif cfg.kind == "sink":
@@ -148,7 +153,7 @@ def make_inputs(cfg, **overrides):
 
 
 def tensor_digest(t: torch.Tensor) -> str:
-    """SHA-256 of a tensor's raw bytes (bf16 tensors are hashed through their int16 view)."""
-    if t.dtype == torch.bfloat16:
+    """SHA-256 of a tensor's raw bytes (16-bit float tensors are hashed through their int16 view)."""
+    if t.dtype in (torch.bfloat16, torch.float16):
         t = t.view(torch.int16)
     return hashlib.sha256(t.contiguous().numpy().tobytes()).hexdigest()

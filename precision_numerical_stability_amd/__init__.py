@@ -1,4 +1,5 @@
-"""BF16 FlashAttention forward/backward for MI355X (gfx950) with the stabilised softmax shift.
+"""BF16 (and FP16) FlashAttention forward/backward for MI355X (gfx950) with the stabilised softmax
+shift.
 
 Thin Python binding over the C ABI of libfa_stable.so (include/fa_stable.h).  The functions named
 like the C entry points (fa_fwd, fa_fwd_ex, fa_bwd, ...) only marshal torch tensors into
@@ -21,7 +22,7 @@ from . import _ffi
 from ._ffi import (FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_PARAM, FA_ERR_ALIGN,
                    FA_ERR_HIP, FA_BWD_DELTA, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL,
                    FA_FWD_COMPENSATED_SUM, FA_CAUSAL_NONE, FA_CAUSAL_TOP_LEFT,
-                   FA_CAUSAL_BOTTOM_RIGHT)
+                   FA_CAUSAL_BOTTOM_RIGHT, FA_ELEM_BF16, FA_ELEM_F16)
 
 _lib = _ffi.load_library()
 
@@ -35,8 +36,9 @@ TIE_ANTICIPATE = 2
 DEFAULT_BETA = 1.25
 
 __all__ = [
-    "fa_fwd", "fa_fwd_ex", "fa_fwd_stats", "fa_fwd_qk", "FA_FWD_COMPENSATED_SUM", "fa_bwd",
-    "fa_bwd_ex", "fa_bwd_qk", "fa_bwd_workspace_bytes", "fa_fwd_kv_block", "fa_probe_mfma_peak",
+    "fa_fwd", "fa_fwd_ex", "fa_fwd_stats", "fa_fwd_qk", "fa_fwd_elem", "FA_FWD_COMPENSATED_SUM",
+    "fa_bwd", "fa_bwd_ex", "fa_bwd_qk", "fa_bwd_elem", "FA_ELEM_BF16", "FA_ELEM_F16",
+    "fa_bwd_workspace_bytes", "fa_fwd_kv_block", "fa_probe_mfma_peak",
     "FA_CAUSAL_NONE", "FA_CAUSAL_TOP_LEFT", "FA_CAUSAL_BOTTOM_RIGHT", "fa_status_str",
     "fa_last_hip_error", "FaError", "forward", "backward", "attention", "STANDARD", "TIE_RULE",
     "TIE_ANTICIPATE", "DEFAULT_BETA", "library_path",
@@ -166,6 +168,36 @@ def fa_fwd_qk(q, k, v, o, lse, dupcnt, ones, smin, smax, causal, scale, beta, st
     _raise(st)
 
 
+_ELEM_OF_DTYPE = {torch.bfloat16: FA_ELEM_BF16, torch.float16: FA_ELEM_F16}
+
+
+def _elem(t, name):
+    if t.dtype not in _ELEM_OF_DTYPE:
+        raise ValueError(f"{name} must be bfloat16 or float16, got {t.dtype}")
+    return _ELEM_OF_DTYPE[t.dtype]
+
+
+def fa_fwd_elem(q, k, v, o, lse, dupcnt, ones, smin, smax, causal, scale, beta, stable_flag,
+                flags=0, stream=None):
+    """Call fa_fwd_elem on torch tensors: as fa_fwd_qk, with q, k, v, o all bfloat16 or all
+    float16 (the element type is taken from q)."""
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    elem = _elem(q, "q")
+    for name, t, n in (("q", q, Nq), ("o", o, Nq), ("k", k, Nk), ("v", v, Nk)):
+        _check(t, name, q.dtype, (B, H, n, d))
+    _check(lse, "lse", torch.float32, (B, H, Nq))
+    for name, t, dt in (("dupcnt", dupcnt, torch.int32), ("ones", ones, torch.int32),
+                        ("smin", smin, torch.float32), ("smax", smax, torch.float32)):
+        if t is not None:
+            _check(t, name, dt, (B, H, Nq))
+    st = _lib.fa_fwd_elem(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dupcnt), _ptr(ones),
+                          _ptr(smin), _ptr(smax), B, H, Nq, Nk, d, int(causal), float(scale),
+                          float(beta), int(stable_flag), int(flags), elem,
+                          _stream_handle(q.device, stream))
+    _raise(st)
+
+
 def fa_fwd(q, k, v, o, lse, causal, scale, beta, stable_flag, stream=None):
     fa_fwd_ex(q, k, v, o, lse, None, None, causal, scale, beta, stable_flag, stream)
 
@@ -204,6 +236,25 @@ def fa_bwd_qk(q, k, v, o, lse, dO, dq, dk, dv, delta_ws, causal, scale, beta=DEF
     _raise(st)
 
 
+def fa_bwd_elem(q, k, v, o, lse, dO, dq, dk, dv, delta_ws, causal, scale, beta=DEFAULT_BETA,
+                stable_flag=STANDARD, stages=_ffi.FA_BWD_ALL, stream=None):
+    """Call fa_bwd_elem on torch tensors: as fa_bwd_qk, with every 16-bit tensor bfloat16 or every
+    one float16 (the element type is taken from q)."""
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    elem = _elem(q, "q")
+    for name, t, n in (("q", q, Nq), ("o", o, Nq), ("dO", dO, Nq), ("dq", dq, Nq), ("k", k, Nk),
+                       ("v", v, Nk), ("dk", dk, Nk), ("dv", dv, Nk)):
+        _check(t, name, q.dtype, (B, H, n, d))
+    _check(lse, "lse", torch.float32, (B, H, Nq))
+    _check(delta_ws, "delta_ws", torch.float32, (B, H, Nq))
+    st = _lib.fa_bwd_elem(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq),
+                          _ptr(dk), _ptr(dv), _ptr(delta_ws), B, H, Nq, Nk, d, int(causal),
+                          float(scale), float(beta), int(stable_flag), int(stages), elem,
+                          _stream_handle(q.device, stream))
+    _raise(st)
+
+
 def fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta_ws, causal, scale, beta=DEFAULT_BETA,
            stable_flag=STANDARD, stream=None):
     """Call fa_bwd on torch tensors (shapes as in fa_fwd_ex; delta_ws fp32 [B,H,N])."""
@@ -225,8 +276,9 @@ def _default_scale(d):
 
 def forward(q, k, v, causal=False, scale=None, beta=DEFAULT_BETA, stable_flag=TIE_RULE,
             stats=False, monitor=False, compensated_sum=False, stream=None):
-    """Allocate outputs and run the forward (fa_fwd_qk: k and v may hold a different number of
-    keys than q has queries; causal 0/False, 1/True (top-left) or 2 (bottom-right)).  Returns
+    """Allocate outputs and run the forward (fa_fwd_elem: bfloat16 or float16 tensors; k and v may
+    hold a different number of keys than q has queries; causal 0/False, 1/True (top-left) or 2
+    (bottom-right)).  Returns
     (o, lse), plus (dupcnt, ones) with stats=True, plus (smin, smax) with monitor=True.
     compensated_sum selects the Kahan row sum."""
     B, H, N, d = q.shape
@@ -241,8 +293,8 @@ def forward(q, k, v, causal=False, scale=None, beta=DEFAULT_BETA, stable_flag=TI
         smin = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
         smax = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     flags = FA_FWD_COMPENSATED_SUM if compensated_sum else 0
-    fa_fwd_qk(q, k, v, o, lse, dup, ones, smin, smax, int(causal), scale, beta, stable_flag, flags,
-              stream)
+    fa_fwd_elem(q, k, v, o, lse, dup, ones, smin, smax, int(causal), scale, beta, stable_flag, flags,
+                stream)
     out = (o, lse)
     if stats:
         out += (dup, ones)
@@ -252,14 +304,14 @@ def forward(q, k, v, causal=False, scale=None, beta=DEFAULT_BETA, stable_flag=TI
 
 
 def backward(q, k, v, o, lse, dO, causal=False, scale=None, stream=None):
-    """Allocate gradients and workspace and run the backward (fa_bwd_qk).  Returns (dq, dk, dv)."""
+    """Allocate gradients and workspace and run the backward (fa_bwd_elem).  Returns (dq, dk, dv)."""
     B, H, N, d = q.shape
     scale = _default_scale(d) if scale is None else scale
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    fa_bwd_qk(q, k, v, o, lse, dO, dq, dk, dv, delta, int(causal), scale, stream=stream)
+    fa_bwd_elem(q, k, v, o, lse, dO, dq, dk, dv, delta, int(causal), scale, stream=stream)
     return dq, dk, dv
 
 
@@ -280,8 +332,8 @@ class _Attention(torch.autograd.Function):
 
 
 def attention(q, k, v, causal=False, scale=None, beta=DEFAULT_BETA, stable_flag=TIE_RULE):
-    """Differentiable attention on bf16 GPU tensors q [B,H,Nq,d], k and v [B,H,Nk,d] (d = 64 or
-    128); causal 0/False, 1/True (top-left) or 2 (bottom-right)."""
+    """Differentiable attention on bfloat16 or float16 GPU tensors q [B,H,Nq,d], k and v [B,H,Nk,d]
+    (d = 64 or 128); causal 0/False, 1/True (top-left) or 2 (bottom-right)."""
     scale = _default_scale(q.shape[-1]) if scale is None else scale
     return _Attention.apply(q.contiguous(), k.contiguous(), v.contiguous(), int(causal),
                             float(scale), float(beta), int(stable_flag))

@@ -23,6 +23,9 @@ FA_CAUSAL_NONE = 0
 FA_CAUSAL_TOP_LEFT = 1
 FA_CAUSAL_BOTTOM_RIGHT = 2
 
+FA_ELEM_BF16 = 0
+FA_ELEM_F16 = 1
+
 FA_BWD_DELTA = 1
 FA_BWD_DKDV = 2
 FA_BWD_DQ = 4
@@ -38,6 +41,8 @@ SIGNATURES = {
     "fa_fwd_stats": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _I, _I, _P]),
     "fa_fwd_qk": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _I, _P]),
     "fa_bwd_qk": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _I, _P]),
+    "fa_fwd_elem": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _I, _I, _P]),
+    "fa_bwd_elem": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _I, _I, _P]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _I, _P]),
     "fa_bwd_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _I, _I, _P]),
     "fa_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),

@@ -15,7 +15,17 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "_lib")
 LIBNAME = "libfa_stable.so"
-SOURCES = ("fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_probe.hip")
+# (source, object name, extra defines).  The kernel files are compiled once per element type:
+# FA_ELEM=0 instantiates the bf16 kernels, FA_ELEM=1 the fp16 ones.
+UNITS = (
+    ("fa_fwd.hip", "fa_fwd_bf16", ("-DFA_ELEM=0",)),
+    ("fa_fwd.hip", "fa_fwd_f16", ("-DFA_ELEM=1",)),
+    ("fa_bwd.hip", "fa_bwd_bf16", ("-DFA_ELEM=0",)),
+    ("fa_bwd.hip", "fa_bwd_f16", ("-DFA_ELEM=1",)),
+    ("fa_api.cpp", "fa_api", ()),
+    ("fa_probe.hip", "fa_probe", ()),
+)
+SOURCES = tuple(sorted({u[0] for u in UNITS}))
 ARCH = "gfx950"
 
 # -packed-fp32-ops keeps the compiler from forming packed fp32 VALU instructions.
@@ -45,9 +55,9 @@ def build(jobs: int = 3, extra=()) -> str:
     os.makedirs(LIBDIR, exist_ok=True)
     objdir = os.path.join(LIBDIR, "obj")
     os.makedirs(objdir, exist_ok=True)
-    objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    objs = [os.path.join(objdir, name + ".o") for _, name, _ in UNITS]
     with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        futs = [ex.submit(_compile, s, o, list(extra)) for s, o in zip(SOURCES, objs)]
+        futs = [ex.submit(_compile, src, o, [*defs, *extra]) for (src, _, defs), o in zip(UNITS, objs)]
         for f in futs:
             f.result()
     out = os.path.join(LIBDIR, LIBNAME)

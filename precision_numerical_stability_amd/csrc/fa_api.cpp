@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdint>
 
+#include "fa_common.hpp"
 #include "fa_launch.hpp"
 
 namespace {
@@ -48,12 +49,13 @@ int hip_status(hipError_t e) {
 
 extern "C" {
 
-int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* dupcnt,
-              int32_t* ones, float* smin, float* smax, int B, int H, int Nq, int Nk, int d, int causal,
-              float scale, float beta, int stable_flag, int flags, void* stream) {
+int fa_fwd_elem(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* dupcnt,
+                int32_t* ones, float* smin, float* smax, int B, int H, int Nq, int Nk, int d, int causal,
+                float scale, float beta, int stable_flag, int flags, int elem, void* stream) {
   const int st = check_common(B, H, Nq, Nk, d, causal, scale, beta, stable_flag);
   if (st != FA_OK) return st;
   if ((flags & ~FA_FWD_COMPENSATED_SUM) != 0) return FA_ERR_PARAM;
+  if (elem != FA_ELEM_BF16 && elem != FA_ELEM_F16) return FA_ERR_PARAM;
   if (int64_t(B) * H == 0 || Nq == 0) return FA_OK;
   if (!q || !o || !lse) return FA_ERR_NULL;
   if (Nk > 0 && (!k || !v)) return FA_ERR_NULL;
@@ -80,8 +82,16 @@ int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, 
   a.beta = beta;
   const bool stats = dupcnt || ones || smin || smax;
   const bool kahan = (flags & FA_FWD_COMPENSATED_SUM) != 0;
-  return hip_status(
-      fa::launch_fwd(a, d, causal != 0, stable_flag, stats, kahan, static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(elem == FA_ELEM_F16 ? fa::launch_fwd<fa::kElemF16>(a, d, causal != 0, stable_flag, stats, kahan, s)
+                                        : fa::launch_fwd<fa::kElemBf16>(a, d, causal != 0, stable_flag, stats, kahan, s));
+}
+
+int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* dupcnt,
+              int32_t* ones, float* smin, float* smax, int B, int H, int Nq, int Nk, int d, int causal,
+              float scale, float beta, int stable_flag, int flags, void* stream) {
+  return fa_fwd_elem(q, k, v, o, lse, dupcnt, ones, smin, smax, B, H, Nq, Nk, d, causal, scale, beta,
+                     stable_flag, flags, FA_ELEM_BF16, stream);
 }
 
 int fa_fwd_stats(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* dupcnt,
@@ -105,12 +115,14 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
                    stream);
 }
 
-int fa_bwd_qk(const void* q, const void* k, const void* v, const void* o, const float* lse,
-              const void* dO, void* dq, void* dk, void* dv, float* delta_ws, int B, int H, int Nq, int Nk,
-              int d, int causal, float scale, float beta, int stable_flag, int stages, void* stream) {
+int fa_bwd_elem(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dO, void* dq, void* dk, void* dv, float* delta_ws, int B, int H, int Nq, int Nk,
+                int d, int causal, float scale, float beta, int stable_flag, int stages, int elem,
+                void* stream) {
   const int st = check_common(B, H, Nq, Nk, d, causal, scale, beta, stable_flag);
   if (st != FA_OK) return st;
   if (stages < 1 || stages > FA_BWD_ALL) return FA_ERR_PARAM;
+  if (elem != FA_ELEM_BF16 && elem != FA_ELEM_F16) return FA_ERR_PARAM;
   if (int64_t(B) * H == 0 || (Nq == 0 && Nk == 0)) return FA_OK;
   if (Nq > 0 && (!q || !o || !lse || !dO || !dq || !delta_ws)) return FA_ERR_NULL;
   if (Nk > 0 && (!k || !v || !dk || !dv)) return FA_ERR_NULL;
@@ -139,17 +151,28 @@ int fa_bwd_qk(const void* q, const void* k, const void* v, const void* o, const 
   a.scale = scale;
   a.sl2 = scale * 1.4426950408889634f;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool f16 = elem == FA_ELEM_F16;
   int rc = FA_OK;
   if (stages & FA_BWD_DELTA) {
-    rc = hip_status(fa::launch_bwd_delta(a, d, s));
+    rc = hip_status(f16 ? fa::launch_bwd_delta<fa::kElemF16>(a, d, s) : fa::launch_bwd_delta<fa::kElemBf16>(a, d, s));
     if (rc != FA_OK) return rc;
   }
   if (stages & FA_BWD_DKDV) {
-    rc = hip_status(fa::launch_bwd_dkdv(a, d, causal != 0, s));
+    rc = hip_status(f16 ? fa::launch_bwd_dkdv<fa::kElemF16>(a, d, causal != 0, s)
+                        : fa::launch_bwd_dkdv<fa::kElemBf16>(a, d, causal != 0, s));
     if (rc != FA_OK) return rc;
   }
-  if (stages & FA_BWD_DQ) rc = hip_status(fa::launch_bwd_dq(a, d, causal != 0, s));
+  if (stages & FA_BWD_DQ)
+    rc = hip_status(f16 ? fa::launch_bwd_dq<fa::kElemF16>(a, d, causal != 0, s)
+                        : fa::launch_bwd_dq<fa::kElemBf16>(a, d, causal != 0, s));
   return rc;
+}
+
+int fa_bwd_qk(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dO, void* dq, void* dk, void* dv, float* delta_ws, int B, int H, int Nq, int Nk,
+              int d, int causal, float scale, float beta, int stable_flag, int stages, void* stream) {
+  return fa_bwd_elem(q, k, v, o, lse, dO, dq, dk, dv, delta_ws, B, H, Nq, Nk, d, causal, scale, beta,
+                     stable_flag, stages, FA_ELEM_BF16, stream);
 }
 
 int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -187,7 +210,7 @@ const char* fa_status_str(int status) {
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: B, H or a sequence length negative, or the problem is too large";
     case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: d must be 64 or 128";
-    case FA_ERR_PARAM: return "FA_ERR_PARAM: causal, scale, beta or stable_flag out of range";
+    case FA_ERR_PARAM: return "FA_ERR_PARAM: causal, scale, beta, stable_flag, flags, stages or elem out of range";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensor pointers must be 16-byte aligned, vectors 4-byte";
     case FA_ERR_HIP: return "FA_ERR_HIP: a HIP call failed (see fa_last_hip_error)";
     default: return "unknown fa_status";

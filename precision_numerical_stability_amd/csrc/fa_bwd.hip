@@ -10,6 +10,10 @@
 //
 // dK/dV and dQ run as two kernels with no atomics: each output tile is owned by exactly one
 // workgroup, so results are deterministic.  All three run on the caller's stream in order.
+//
+// Tensors hold 16-bit elements (bf16 or fp16, the template parameter E; this file is compiled
+// once per element type, FA_ELEM); P and dS are rounded to that type for their products, and
+// every other step is fp32.
 #include <type_traits>
 
 #include <climits>
@@ -17,14 +21,18 @@
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
+#ifndef FA_ELEM
+#error "FA_ELEM (the element type this translation unit instantiates) must be defined"
+#endif
+
 namespace fa {
 
 constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------------------------------------
-// delta[row] = sum_c dO[row, c] * O[row, c], bf16 inputs, fp32 arithmetic.  HBM-bound: one
+// delta[row] = sum_c dO[row, c] * O[row, c], 16-bit inputs, fp32 arithmetic.  HBM-bound: one
 // 16-byte load of O and of dO per thread, D / 8 threads per row.
-template <int D>
+template <int E, int D>
 __global__ __launch_bounds__(kThreads) void delta_kernel(BwdArgs a) {
   constexpr int TPR = D / 8;
   constexpr int RPB = kThreads / TPR;
@@ -38,14 +46,10 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(BwdArgs a) {
     const i32x4 gv = *reinterpret_cast<const i32x4*>(a.dO + row * D + 8 * c);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t ow = (uint32_t)ov[i];
-      const uint32_t gw = (uint32_t)gv[i];
-      const float o_lo = __builtin_bit_cast(float, ow << 16);
-      const float o_hi = __builtin_bit_cast(float, ow & 0xFFFF0000u);
-      const float g_lo = __builtin_bit_cast(float, gw << 16);
-      const float g_hi = __builtin_bit_cast(float, gw & 0xFFFF0000u);
-      acc = fmaf(o_lo, g_lo, acc);
-      acc = fmaf(o_hi, g_hi, acc);
+      const f32x2 o2 = unpack2<E>((uint32_t)ov[i]);
+      const f32x2 g2 = unpack2<E>((uint32_t)gv[i]);
+      acc = fmaf(o2[0], g2[0], acc);
+      acc = fmaf(o2[1], g2[1], acc);
     }
   }
 #pragma unroll
@@ -63,22 +67,22 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(BwdArgs a) {
 constexpr int kDqBc = 64;
 constexpr int kDqBr = 128;
 
-template <int D>
+template <int E, int D>
 __device__ __forceinline__ void dq_sdp(const uint16_t* tK, const uint16_t* tV, int kr, int l32, int hh,
-                                       const bf16x8 (&qf)[D / 16], const bf16x8 (&gf)[D / 16], f32x16& s,
+                                       const e16x8 (&qf)[D / 16], const e16x8 (&gf)[D / 16], f32x16& s,
                                        f32x16& dp) {
   s = zero16();
   dp = zero16();
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    const bf16x8 kf = lds_read_row8<D>(tK, kr + l32, 16 * ks + 8 * hh);
-    const bf16x8 vf = lds_read_row8<D>(tV, kr + l32, 16 * ks + 8 * hh);
-    s = mfma32x32x16(kf, qf[ks], s);
-    dp = mfma32x32x16(vf, gf[ks], dp);
+    const e16x8 kf = lds_read_row8<D>(tK, kr + l32, 16 * ks + 8 * hh);
+    const e16x8 vf = lds_read_row8<D>(tV, kr + l32, 16 * ks + 8 * hh);
+    s = mfma32x32x16<E>(kf, qf[ks], s);
+    dp = mfma32x32x16<E>(vf, gf[ks], dp);
   }
 }
 
-template <bool MASK, bool CAUSAL>
+template <int E, bool MASK, bool CAUSAL>
 __device__ __forceinline__ void dq_grad(const f32x16& s, const f32x16& dp, int key0, int qrow, int nk, int hh,
                                         float sl2, float lse2, float dlt, uint32_t (&pds)[8]) {
 #pragma unroll
@@ -99,25 +103,25 @@ __device__ __forceinline__ void dq_grad(const f32x16& s, const f32x16& dp, int k
       }
       ds2[u] = p * (dp[rr] - dlt);
     }
-    pds[r >> 1] = pack_bf16x2(ds2[0], ds2[1]);
+    pds[r >> 1] = pack2<E>(ds2[0], ds2[1]);
   }
 }
 
-template <int D>
+template <int E, int D>
 __device__ __forceinline__ void dq_accum(const uint16_t* tK, int kr, int lane, const uint32_t (&pds)[8],
                                          f32x16 (&acc)[D / 32]) {
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    const bf16x8 db = make_bf16x8(pds[4 * half], pds[4 * half + 1], pds[4 * half + 2], pds[4 * half + 3]);
+    const e16x8 db = make_e16x8(pds[4 * half], pds[4 * half + 1], pds[4 * half + 2], pds[4 * half + 3]);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
-      const bf16x8 kt = lds_read_col8_tr<D>(tK, kr + 16 * half, 32 * dt, lane);
-      acc[dt] = mfma32x32x16(kt, db, acc[dt]);
+      const e16x8 kt = lds_read_col8_tr<D>(tK, kr + 16 * half, 32 * dt, lane);
+      acc[dt] = mfma32x32x16<E>(kt, db, acc[dt]);
     }
   }
 }
 
-template <int D, bool CAUSAL>
+template <int E, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
   constexpr int BC = kDqBc, BR = kDqBr, KS = D / 16, DT = D / 32;
   static_assert(BC == 64, "the block body handles two 32-key halves");
@@ -142,14 +146,14 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
   const int qrow = q0 + wave * 32 + l32;
   const int qsrc = min(qrow, Nq - 1);
 
-  bf16x8 qf[KS], gf[KS];
+  e16x8 qf[KS], gf[KS];
   {
     const uint16_t* qs = a.q + qoff + (int64_t)qsrc * D + 8 * hh;
     const uint16_t* gs = a.dO + qoff + (int64_t)qsrc * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      qf[ks] = as_bf16x8(*reinterpret_cast<const i32x4*>(qs + 16 * ks));
-      gf[ks] = as_bf16x8(*reinterpret_cast<const i32x4*>(gs + 16 * ks));
+      qf[ks] = as_e16x8(*reinterpret_cast<const i32x4*>(qs + 16 * ks));
+      gf[ks] = as_e16x8(*reinterpret_cast<const i32x4*>(gs + 16 * ks));
     }
   }
   const float lse2 = a.lse[(int64_t)bh * Nq + qsrc] * kLog2e;
@@ -191,19 +195,19 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
     uint32_t pds0[8], pds1[8];
     f32x16 s1, dp1;
     __builtin_amdgcn_sched_barrier(0);
-    dq_sdp<D>(tK, tV, 0, l32, hh, qf, gf, s, dp);
+    dq_sdp<E, D>(tK, tV, 0, l32, hh, qf, gf, s, dp);
     sched_reads_ahead<2 * KS, 1, 4>();
     __builtin_amdgcn_sched_barrier(0);
     // dS of the first half on the vector ALUs while the second half's S/dP run on the matrix cores.
-    dq_sdp<D>(tK, tV, 32, l32, hh, qf, gf, s1, dp1);
-    dq_grad<MASK, CAUSAL>(s, dp, kv0 - a.coff, qrow, Nk - a.coff, hh, a.sl2, lse2, dlt, pds0);
+    dq_sdp<E, D>(tK, tV, 32, l32, hh, qf, gf, s1, dp1);
+    dq_grad<E, MASK, CAUSAL>(s, dp, kv0 - a.coff, qrow, Nk - a.coff, hh, a.sl2, lse2, dlt, pds0);
     sched_reads_ahead_valu<2 * KS, 1, 4, 4>();
     __builtin_amdgcn_sched_barrier(0);
-    dq_grad<MASK, CAUSAL>(s1, dp1, kv0 + 32 - a.coff, qrow, Nk - a.coff, hh, a.sl2, lse2, dlt, pds1);
-    dq_accum<D>(tK, 0, lane, pds0, acc);
+    dq_grad<E, MASK, CAUSAL>(s1, dp1, kv0 + 32 - a.coff, qrow, Nk - a.coff, hh, a.sl2, lse2, dlt, pds1);
+    dq_accum<E, D>(tK, 0, lane, pds0, acc);
     sched_reads_ahead_valu<2 * DT, 2, 3, 8>();
     __builtin_amdgcn_sched_barrier(0);
-    dq_accum<D>(tK, 32, lane, pds1, acc);
+    dq_accum<E, D>(tK, 32, lane, pds1, acc);
     sched_reads_ahead<2 * DT, 2, 3>();
     __builtin_amdgcn_sched_barrier(0);
     wait_vm0();
@@ -232,8 +236,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
       for (int rr = 0; rr < 4; ++rr) {
         const int d0 = 32 * dt + 8 * rr + 4 * hh;
         i32x2 w;
-        w[0] = (int)pack_bf16x2(acc[dt][4 * rr] * a.scale, acc[dt][4 * rr + 1] * a.scale);
-        w[1] = (int)pack_bf16x2(acc[dt][4 * rr + 2] * a.scale, acc[dt][4 * rr + 3] * a.scale);
+        w[0] = (int)pack2<E>(acc[dt][4 * rr] * a.scale, acc[dt][4 * rr + 1] * a.scale);
+        w[1] = (int)pack2<E>(acc[dt][4 * rr + 2] * a.scale, acc[dt][4 * rr + 3] * a.scale);
         *reinterpret_cast<i32x2*>(dst + d0) = w;
       }
   }
@@ -253,8 +257,8 @@ constexpr int kDkvBk = 128;
 
 template <int D>
 struct DkvFrags {
-  bf16x8 k[D / 16];
-  bf16x8 v[D / 16];
+  e16x8 k[D / 16];
+  e16x8 v[D / 16];
 };
 
 // The block's MFMA stream, in time order, is 2 SB phases of L steps (L = 2 D/16 = 4 D/32):
@@ -314,7 +318,7 @@ struct DkvSched {
 // S = Q K^T and dP = dO V^T recomputed per 32-query sub-block.  Operand reads run DEPTH steps
 // ahead of their MFMA through a ring of registers; every step is fenced so the order above is the
 // order the instructions issue in.
-template <int D, bool CAUSAL, bool MASK>
+template <int E, int D, bool CAUSAL, bool MASK>
 __device__ __forceinline__ void dkdv_block(const uint16_t* tQ, const uint16_t* tG, const float* tL,
                                            const float* tD, int q0, int Nq, int coff, int key, int lane, float sl2,
                                            const DkvFrags<D>& f, f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
@@ -326,7 +330,7 @@ __device__ __forceinline__ void dkdv_block(const uint16_t* tQ, const uint16_t* t
   const int hh = lane >> 5;
   f32x16 s[2], dp[2];
   uint32_t pp[2][8], pd[2][8];
-  bf16x8 ring[RING];
+  e16x8 ring[RING];
   float4 lsl[2][2], dsl[2][2];  // [half slot][row group] LSE (log2 units) and delta vectors
   float pt0 = 0.f, dt0 = 0.f;   // first element of the pair being packed
 
@@ -354,26 +358,26 @@ __device__ __forceinline__ void dkdv_block(const uint16_t* tQ, const uint16_t* t
   auto mfma_step = [&](auto kc) __attribute__((always_inline)) {
     constexpr int k = decltype(kc)::value;
     constexpr int t = S::sub(k), i = k % S::L, c = t & 1;
-    const bf16x8 op = ring[k % RING];
+    const e16x8 op = ring[k % RING];
     if constexpr (S::is_sdp(k)) {
       constexpr int ks = i >> 1;
       if constexpr ((i & 1) == 0) {
-        s[c] = mfma32x32x16(op, f.k[ks], ks == 0 ? zero16() : s[c]);
+        s[c] = mfma32x32x16<E>(op, f.k[ks], ks == 0 ? zero16() : s[c]);
       } else {
-        dp[c] = mfma32x32x16(op, f.v[ks], ks == 0 ? zero16() : dp[c]);
+        dp[c] = mfma32x32x16<E>(op, f.v[ks], ks == 0 ? zero16() : dp[c]);
       }
     } else {
       constexpr int half = i / (2 * DT), dt = (i >> 1) % DT, o4 = 4 * half;
       if constexpr ((i & 1) == 0) {
-        dv[dt] = mfma32x32x16(op, make_bf16x8(pp[c][o4], pp[c][o4 + 1], pp[c][o4 + 2], pp[c][o4 + 3]), dv[dt]);
+        dv[dt] = mfma32x32x16<E>(op, make_e16x8(pp[c][o4], pp[c][o4 + 1], pp[c][o4 + 2], pp[c][o4 + 3]), dv[dt]);
       } else {
-        dk[dt] = mfma32x32x16(op, make_bf16x8(pd[c][o4], pd[c][o4 + 1], pd[c][o4 + 2], pd[c][o4 + 3]), dk[dt]);
+        dk[dt] = mfma32x32x16<E>(op, make_e16x8(pd[c][o4], pd[c][o4 + 1], pd[c][o4 + 2], pd[c][o4 + 3]), dk[dt]);
       }
     }
   };
   // Element e of half g: P = exp2(S scale log2e - LSE log2e), dS = P (dP - delta), masked queries
   // (past Nq, or, when causal, before key - coff, the first query that sees this lane's key)
-  // give zero; pairs are packed to bf16.
+  // give zero; pairs are packed to the element type.
   auto grad_elem = [&](auto mc) __attribute__((always_inline)) {
     constexpr int m = decltype(mc)::value;
     constexpr int g = m >> 3, e = m & 7;
@@ -398,8 +402,8 @@ __device__ __forceinline__ void dkdv_block(const uint16_t* tQ, const uint16_t* t
       pt0 = p;
       dt0 = ds;
     } else {
-      pp[c][2 * rq + (u >> 1)] = pack_bf16x2(pt0, p);
-      pd[c][2 * rq + (u >> 1)] = pack_bf16x2(dt0, ds);
+      pp[c][2 * rq + (u >> 1)] = pack2<E>(pt0, p);
+      pd[c][2 * rq + (u >> 1)] = pack2<E>(dt0, ds);
     }
   };
 
@@ -420,7 +424,7 @@ __device__ __forceinline__ void dkdv_block(const uint16_t* tQ, const uint16_t* t
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, bool CAUSAL>
+template <int E, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   constexpr int BQ = kDkvBq, BK = kDkvBk, KS = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BQ * D];
@@ -454,8 +458,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
     const uint16_t* vs_ = a.v + koff + (int64_t)ksrc * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      f.k[ks] = as_bf16x8(*reinterpret_cast<const i32x4*>(ks_ + 16 * ks));
-      f.v[ks] = as_bf16x8(*reinterpret_cast<const i32x4*>(vs_ + 16 * ks));
+      f.k[ks] = as_e16x8(*reinterpret_cast<const i32x4*>(ks_ + 16 * ks));
+      f.v[ks] = as_e16x8(*reinterpret_cast<const i32x4*>(vs_ + 16 * ks));
     }
   }
 
@@ -506,7 +510,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
       st.issue(Gg, q0 + BQ, Nq, aG + (buf ^ 1) * kTileBytes);
       load_rows(i + 1);
     }
-    dkdv_block<D, CAUSAL, MASK>(sQ[buf], sG[buf], sL[buf], sD[buf], q0, Nq, a.coff, key, lane, a.sl2, f, dk, dv);
+    dkdv_block<E, D, CAUSAL, MASK>(sQ[buf], sG[buf], sL[buf], sD[buf], q0, Nq, a.coff, key, lane, a.sl2, f, dk, dv);
     if (has_next) store_rows(buf ^ 1);
     wait_vm0();
     __syncthreads();
@@ -540,10 +544,10 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
       for (int rr = 0; rr < 4; ++rr) {
         const int d0 = 32 * dt + 8 * rr + 4 * hh;
         i32x2 wk, wv;
-        wk[0] = (int)pack_bf16x2(dk[dt][4 * rr] * a.scale, dk[dt][4 * rr + 1] * a.scale);
-        wk[1] = (int)pack_bf16x2(dk[dt][4 * rr + 2] * a.scale, dk[dt][4 * rr + 3] * a.scale);
-        wv[0] = (int)pack_bf16x2(dv[dt][4 * rr], dv[dt][4 * rr + 1]);
-        wv[1] = (int)pack_bf16x2(dv[dt][4 * rr + 2], dv[dt][4 * rr + 3]);
+        wk[0] = (int)pack2<E>(dk[dt][4 * rr] * a.scale, dk[dt][4 * rr + 1] * a.scale);
+        wk[1] = (int)pack2<E>(dk[dt][4 * rr + 2] * a.scale, dk[dt][4 * rr + 3] * a.scale);
+        wv[0] = (int)pack2<E>(dv[dt][4 * rr], dv[dt][4 * rr + 1]);
+        wv[1] = (int)pack2<E>(dv[dt][4 * rr + 2], dv[dt][4 * rr + 3]);
         *reinterpret_cast<i32x2*>(dkr + d0) = wk;
         *reinterpret_cast<i32x2*>(dvr + d0) = wv;
       }
@@ -551,44 +555,51 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+template <int E>
 hipError_t launch_bwd_delta(BwdArgs a, int d, hipStream_t s) {
   const int64_t total = (int64_t)a.BH * a.Nq;
   if (total == 0) return hipSuccess;
   const int rpb = kThreads / (d / 8);
   const int64_t grid = (total + rpb - 1) / rpb;
   if (d == 64)
-    hipLaunchKernelGGL(delta_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((delta_kernel<E, 64>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(delta_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((delta_kernel<E, 128>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
+template <int E>
 hipError_t launch_bwd_dq(BwdArgs a, int d, bool causal, hipStream_t s) {
   a.n_tiles = (a.Nq + kDqBr - 1) / kDqBr;
   if (a.n_tiles == 0 || a.BH == 0) return hipSuccess;
   const dim3 grid(a.n_tiles * a.BH);
   if (d == 64) {
-    if (causal) hipLaunchKernelGGL((dq_kernel<64, true>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((dq_kernel<64, false>), grid, dim3(kThreads), 0, s, a);
+    if (causal) hipLaunchKernelGGL((dq_kernel<E, 64, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((dq_kernel<E, 64, false>), grid, dim3(kThreads), 0, s, a);
   } else {
-    if (causal) hipLaunchKernelGGL((dq_kernel<128, true>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((dq_kernel<128, false>), grid, dim3(kThreads), 0, s, a);
+    if (causal) hipLaunchKernelGGL((dq_kernel<E, 128, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((dq_kernel<E, 128, false>), grid, dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }
 
+template <int E>
 hipError_t launch_bwd_dkdv(BwdArgs a, int d, bool causal, hipStream_t s) {
   a.n_tiles = (a.Nk + kDkvBk - 1) / kDkvBk;
   if (a.n_tiles == 0 || a.BH == 0) return hipSuccess;
   const dim3 grid(a.n_tiles * a.BH);
   if (d == 64) {
-    if (causal) hipLaunchKernelGGL((dkdv_kernel<64, true>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((dkdv_kernel<64, false>), grid, dim3(kThreads), 0, s, a);
+    if (causal) hipLaunchKernelGGL((dkdv_kernel<E, 64, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((dkdv_kernel<E, 64, false>), grid, dim3(kThreads), 0, s, a);
   } else {
-    if (causal) hipLaunchKernelGGL((dkdv_kernel<128, true>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((dkdv_kernel<128, false>), grid, dim3(kThreads), 0, s, a);
+    if (causal) hipLaunchKernelGGL((dkdv_kernel<E, 128, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((dkdv_kernel<E, 128, false>), grid, dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }
+
+template hipError_t launch_bwd_delta<FA_ELEM>(BwdArgs, int, hipStream_t);
+template hipError_t launch_bwd_dq<FA_ELEM>(BwdArgs, int, bool, hipStream_t);
+template hipError_t launch_bwd_dkdv<FA_ELEM>(BwdArgs, int, bool, hipStream_t);
 
 }  // namespace fa

@@ -1,7 +1,8 @@
-// Device primitives for the gfx950 attention kernels: MFMA wrappers, bf16 packing, swizzled LDS
-// tiles, the LDS transpose read, and half-wave reductions.
+// Device primitives for the gfx950 attention kernels: MFMA wrappers and fp32 -> 16-bit packing for
+// the two element types (bf16, fp16), swizzled LDS tiles, the LDS transpose read, and half-wave
+// reductions.
 //
-// Register layouts (v_mfma_f32_32x32x16_bf16, one wave of 64 lanes, h = lane / 32):
+// Register layouts (v_mfma_f32_32x32x16_bf16 and _f16 alike, one wave of 64 lanes, h = lane / 32):
 //   A operand (32 x 16):  lane l holds A[l % 32][8h .. 8h + 7]
 //   B operand (16 x 32):  lane l holds B[8h .. 8h + 7][l % 32]
 //   C/D (32 x 32 fp32):   lane l, register r holds C[8 (r / 4) + 4 h + (r % 4)][l % 32]
@@ -24,8 +25,12 @@
 
 namespace fa {
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+// Eight 16-bit elements: one MFMA operand per lane.  The storage is typed bf16; with fp16 elements
+// the same bits are reinterpreted at the MFMA.
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 e16x8;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
@@ -36,10 +41,25 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr uint16_t kBf16One = 0x3F80;
 
-__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+// Element type of q, k, v, o, dO and the gradients, and of the 16-bit operands the products take
+// (P^ and dS are rounded to it too).  Arithmetic is fp32 for both.
+constexpr int kElemBf16 = 0;
+constexpr int kElemF16 = 1;
+
+// Bit pattern of 1.0 in the element type.
+template <int E>
+constexpr uint16_t elem_one() { return E == kElemF16 ? 0x3C00 : 0x3F80; }
+
+// C += A B, 32 x 32 x 16, fp32 accumulation, operands of element type E.
+template <int E>
+__device__ __forceinline__ f32x16 mfma32x32x16(e16x8 a, e16x8 b, f32x16 c) {
+  if constexpr (E == kElemF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
 }
 
 __device__ __forceinline__ f32x16 zero16() {
@@ -49,17 +69,34 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-// Two fp32 -> packed bf16 pair (round to nearest even), low half = a.
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  bf16x2 r = __builtin_convertvector((f32x2){a, b}, bf16x2);
-  return __builtin_bit_cast(uint32_t, r);
+// Two fp32 -> a packed pair of the element type (round to nearest even; fp16 overflows to inf),
+// low half = a.
+template <int E>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (E == kElemF16) {
+    f16x2 r = __builtin_convertvector((f32x2){a, b}, f16x2);
+    return __builtin_bit_cast(uint32_t, r);
+  } else {
+    bf16x2 r = __builtin_convertvector((f32x2){a, b}, bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
+  }
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(i32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+// The two elements of a packed pair as fp32 (exact): low half, high half.
+template <int E>
+__device__ __forceinline__ f32x2 unpack2(uint32_t w) {
+  if constexpr (E == kElemF16) {
+    return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+  } else {
+    return (f32x2){__builtin_bit_cast(float, w << 16), __builtin_bit_cast(float, w & 0xFFFF0000u)};
+  }
+}
 
-__device__ __forceinline__ bf16x8 make_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+__device__ __forceinline__ e16x8 as_e16x8(i32x4 v) { return __builtin_bit_cast(e16x8, v); }
+
+__device__ __forceinline__ e16x8 make_e16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   i32x4 v = {(int)a, (int)b, (int)c, (int)d};
-  return __builtin_bit_cast(bf16x8, v);
+  return __builtin_bit_cast(e16x8, v);
 }
 
 // Reductions over the two 32-lane halves of a wave: lane l and lane l ^ 32 both receive the
@@ -89,7 +126,7 @@ __device__ __forceinline__ int halves_sum_i(int x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------------------------
-// Swizzled row-major [rows][D] bf16 tiles in LDS.  The 16-byte chunk c of row r is stored at
+// Swizzled row-major [rows][D] tiles of 16-bit elements in LDS.  The 16-byte chunk c of row r is stored at
 // chunk c ^ f(r), with f an XOR-linear map of the low four bits r0..r3 of the row:
 //   d = 128 (16 chunks per row):  f = 4 r0 ^ 10 r1 ^ 1 r2 ^ 8 r3
 //   d = 64  ( 8 chunks per row):  f = 2 r0 ^  4 r1 ^ 1 r2 ^ 2 r3
@@ -118,14 +155,14 @@ __device__ __forceinline__ int lds_off(int row, int col) {
 
 // 16-byte operand read: row `row`, columns col .. col + 7 (col a multiple of 8).
 template <int D>
-__device__ __forceinline__ bf16x8 lds_read_row8(const uint16_t* tile, int row, int col) {
-  return as_bf16x8(*reinterpret_cast<const i32x4*>(tile + lds_off<D>(row, col)));
+__device__ __forceinline__ e16x8 lds_read_row8(const uint16_t* tile, int row, int col) {
+  return as_e16x8(*reinterpret_cast<const i32x4*>(tile + lds_off<D>(row, col)));
 }
 
 // Transposed operand read: this lane receives column (col0 + (lane % 32)) at the eight rows
 // row0 + 4h + {0,1,2,3} and row0 + 8 + 4h + {0,1,2,3} (h = lane / 32), in that slot order.
 template <int D>
-__device__ __forceinline__ bf16x8 lds_read_col8_tr(const uint16_t* tile, int row0, int col0, int lane) {
+__device__ __forceinline__ e16x8 lds_read_col8_tr(const uint16_t* tile, int row0, int col0, int lane) {
   const int s = lane & 15;
   const int g = lane >> 4;
   const int h = lane >> 5;
@@ -137,7 +174,7 @@ __device__ __forceinline__ bf16x8 lds_read_col8_tr(const uint16_t* tile, int row
   i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p2));
   i32x2 a = __builtin_bit_cast(i32x2, lo);
   i32x2 b = __builtin_bit_cast(i32x2, hi);
-  return make_bf16x8((uint32_t)a[0], (uint32_t)a[1], (uint32_t)b[0], (uint32_t)b[1]);
+  return make_e16x8((uint32_t)a[0], (uint32_t)a[1], (uint32_t)b[0], (uint32_t)b[1]);
 }
 
 // Byte address in LDS of a __shared__ object.  Take it from the array itself (not from a pointer
@@ -147,7 +184,7 @@ __device__ __forceinline__ uint32_t lds_addr(T* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) T*)p;
 }
 
-// Direct global -> LDS staging of a ROWS x D bf16 tile with buffer_load_dwordx4 ... lds: each
+// Direct global -> LDS staging of a ROWS x D tile of 16-bit elements with buffer_load_dwordx4 ... lds: each
 // lane moves 16 bytes straight into LDS (lane l of a wave writes at M0 + 16 l), so no registers
 // hold the tile in flight.  The swizzle is applied on the global side: LDS chunk position p
 // (row p / (D/8), physical chunk p % (D/8)) is fed from logical chunk physical ^ swz(row).  The

@@ -4,7 +4,9 @@
 // Follows the online softmax of the BF16 Flash Attention article (ijyty.com/news/896914) §2.1 and
 // the repeated-maximum shift of its §4.1, with the precision schedule of "Flash Attention低精度
 // 训练稳定性优化实践" (jsqmd.com/news/761560) §3.2: Q K^T accumulated in fp32, softmax in fp32,
-// P^ rounded to bf16 for the product with V.
+// P^ rounded to the 16-bit element type for the product with V.  That article names both 16-bit
+// formats; the element type (bf16 or fp16) is a template parameter, and this file is compiled once
+// per element type (FA_ELEM).
 //
 // Work split: one workgroup of 8 waves per (query tile of 256 rows, head).  Each wave owns 32
 // queries and computes S^T = K Q^T, so each lane owns one query column: its row max, repeat count
@@ -28,6 +30,10 @@
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
+#ifndef FA_ELEM
+#error "FA_ELEM (the element type this translation unit instantiates) must be defined"
+#endif
+
 namespace fa {
 
 // Keys per block: 128 when causal; 64 otherwise (the non-causal instances spill at 128).
@@ -45,10 +51,10 @@ struct RowState {
   float lsum;     // this half-wave's share of the row sum
   float lcomp;    // its compensation term (compensated-sum variant): lost low-order part, negated
   float run_min;  // running min of the raw dot products over visible keys (diagnostics variant)
-  int n_ones;     // exact-1.0 bf16 P^ values seen (stats variant)
+  int n_ones;     // exact-1.0 16-bit P^ values seen (stats variant)
 };
 
-template <int D, bool CAUSAL, int MODE, bool STATS, bool KAHAN>
+template <int E, int D, bool CAUSAL, int MODE, bool STATS, bool KAHAN>
 __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   constexpr int BC = fwd_bc<CAUSAL>(), BR = kFwdBr, KS = D / 16, DT = D / 32, KB = BC / 32;
   // Mode 1 needs only whether the running maximum repeats: without the diagnostics that is
@@ -80,11 +86,11 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   const int qrow = qw0 + l32;      // this lane's query (causal: it sees keys up to qrow + coff)
 
   // Q^T as the B operand: lane holds Q[qrow][16 ks + 8 hh .. + 7].
-  bf16x8 qf[KS];
+  e16x8 qf[KS];
   {
     const uint16_t* src = Qg + (int64_t)min(qrow, Nq - 1) * D + 8 * hh;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const i32x4*>(src + 16 * ks));
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = as_e16x8(*reinterpret_cast<const i32x4*>(src + 16 * ks));
   }
 
   int n_kv = (Nk + BC - 1) / BC;
@@ -120,7 +126,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   constexpr int KK = BC / 16;
   constexpr int NPV = DT * KK, NSS = KB * KS;
   constexpr int MDEPTH = 4, MRING = MDEPTH + 1;
-  bf16x8 mring[MRING];
+  e16x8 mring[MRING];
   auto m_read = [&](auto kc, const uint16_t* tV, const uint16_t* tK) __attribute__((always_inline)) {
     constexpr int k = decltype(kc)::value;
     if constexpr (k < NPV) {
@@ -133,10 +139,10 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   };
   auto m_step = [&](auto kc) __attribute__((always_inline)) {
     constexpr int k = decltype(kc)::value;
-    const bf16x8 op = mring[k % MRING];
+    const e16x8 op = mring[k % MRING];
     if constexpr (k < NPV) {
       constexpr int dt = k / KK, kk = k % KK, o4 = (kk & 1) * 4;
-      oacc[dt] = mfma32x32x16(op, make_bf16x8(pk[kk >> 1][o4], pk[kk >> 1][o4 + 1], pk[kk >> 1][o4 + 2],
+      oacc[dt] = mfma32x32x16<E>(op, make_e16x8(pk[kk >> 1][o4], pk[kk >> 1][o4 + 1], pk[kk >> 1][o4 + 2],
                                               pk[kk >> 1][o4 + 3]), oacc[dt]);
       if constexpr (dt + 1 < DT) {
         constexpr int per = 16 / KK;
@@ -145,7 +151,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
       }
     } else {
       constexpr int i = k - NPV, kb = i / KS, ks = i % KS;
-      s[kb] = mfma32x32x16(op, qf[ks], ks == 0 ? zero16() : s[kb]);
+      s[kb] = mfma32x32x16<E>(op, qf[ks], ks == 0 ? zero16() : s[kb]);
     }
   };
   auto m_stream = [&](auto k0c, auto k1c, const uint16_t* tV, const uint16_t* tK) __attribute__((always_inline)) {
@@ -273,7 +279,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
     }
     const float alpha = fast_exp2(rs.m2 - m2_new);
     rs.m2 = m2_new;
-    // P^ = exp2(S * scale * log2e - m), its row sum, and its bf16 packing for the V product.
+    // P^ = exp2(S * scale * log2e - m), its row sum, and its 16-bit packing for the V product.
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -282,9 +288,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
         const float p0 = fast_exp2(fmaf(s[kb][r], a.sl2, -m2_new));
         const float p1 = fast_exp2(fmaf(s[kb][r + 1], a.sl2, -m2_new));
         psum += p0 + p1;
-        const uint32_t w = pack_bf16x2(p0, p1);
+        const uint32_t w = pack2<E>(p0, p1);
         pk[kb][r >> 1] = w;
-        if (STATS) rs.n_ones += ((w & 0xFFFFu) == kBf16One) + ((w >> 16) == kBf16One);
+        if (STATS) rs.n_ones += ((w & 0xFFFFu) == elem_one<E>()) + ((w >> 16) == elem_one<E>());
       }
     if constexpr (KAHAN) {
       // Compensated running sum: the previous sum and its compensation scale by alpha together;
@@ -350,8 +356,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) x[u] = empty ? 0.f : oacc[dt][4 * rr + u] * inv;
         i32x2 w;
-        w[0] = (int)pack_bf16x2(x[0], x[1]);
-        w[1] = (int)pack_bf16x2(x[2], x[3]);
+        w[0] = (int)pack2<E>(x[0], x[1]);
+        w[1] = (int)pack2<E>(x[2], x[3]);
         *reinterpret_cast<i32x2*>(orow + d0) = w;
       }
     if (hh == 0) {
@@ -367,40 +373,46 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   }
 }
 
-template <int D, bool CAUSAL, int MODE, bool STATS, bool KAHAN>
+template <int E, int D, bool CAUSAL, int MODE, bool STATS, bool KAHAN>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const int grid = a.n_tiles * a.BH;
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, MODE, STATS, KAHAN>), dim3(grid), dim3(kFwdThreads), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, MODE, STATS, KAHAN>), dim3(grid), dim3(kFwdThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool STATS, bool KAHAN>
+template <int E, int D, bool CAUSAL, bool STATS, bool KAHAN>
 static hipError_t launch_fwd_m(const FwdArgs& a, int mode, hipStream_t s) {
-  if (mode == 0) return launch_fwd_t<D, CAUSAL, 0, STATS, KAHAN>(a, s);
-  if (mode == 1) return launch_fwd_t<D, CAUSAL, 1, STATS, KAHAN>(a, s);
-  return launch_fwd_t<D, CAUSAL, 2, STATS, KAHAN>(a, s);
+  if (mode == 0) return launch_fwd_t<E, D, CAUSAL, 0, STATS, KAHAN>(a, s);
+  if (mode == 1) return launch_fwd_t<E, D, CAUSAL, 1, STATS, KAHAN>(a, s);
+  return launch_fwd_t<E, D, CAUSAL, 2, STATS, KAHAN>(a, s);
 }
 
-template <int D, bool CAUSAL>
+template <int E, int D, bool CAUSAL>
 static hipError_t launch_fwd_mode(const FwdArgs& a, int mode, bool stats, bool kahan, hipStream_t s) {
-  if (stats) return kahan ? launch_fwd_m<D, CAUSAL, true, true>(a, mode, s) : launch_fwd_m<D, CAUSAL, true, false>(a, mode, s);
-  return kahan ? launch_fwd_m<D, CAUSAL, false, true>(a, mode, s) : launch_fwd_m<D, CAUSAL, false, false>(a, mode, s);
+  if (stats)
+    return kahan ? launch_fwd_m<E, D, CAUSAL, true, true>(a, mode, s) : launch_fwd_m<E, D, CAUSAL, true, false>(a, mode, s);
+  return kahan ? launch_fwd_m<E, D, CAUSAL, false, true>(a, mode, s) : launch_fwd_m<E, D, CAUSAL, false, false>(a, mode, s);
 }
 
+#if FA_ELEM == 0
 int fwd_kv_block(int d, bool causal) {
   if (d != 64 && d != 128) return 0;
   return causal ? fwd_bc<true>() : fwd_bc<false>();
 }
 int fwd_q_block(int d) { return (d == 64 || d == 128) ? kFwdBr : 0; }
+#endif
 
+template <int E>
 hipError_t launch_fwd(FwdArgs a, int d, bool causal, int mode, bool stats, bool kahan, hipStream_t s) {
   a.n_tiles = (a.Nq + kFwdBr - 1) / kFwdBr;
   if (a.n_tiles == 0 || a.BH == 0) return hipSuccess;
   if (d == 64)
-    return causal ? launch_fwd_mode<64, true>(a, mode, stats, kahan, s)
-                  : launch_fwd_mode<64, false>(a, mode, stats, kahan, s);
-  return causal ? launch_fwd_mode<128, true>(a, mode, stats, kahan, s)
-                : launch_fwd_mode<128, false>(a, mode, stats, kahan, s);
+    return causal ? launch_fwd_mode<E, 64, true>(a, mode, stats, kahan, s)
+                  : launch_fwd_mode<E, 64, false>(a, mode, stats, kahan, s);
+  return causal ? launch_fwd_mode<E, 128, true>(a, mode, stats, kahan, s)
+                : launch_fwd_mode<E, 128, false>(a, mode, stats, kahan, s);
 }
+
+template hipError_t launch_fwd<FA_ELEM>(FwdArgs, int, bool, int, bool, bool, hipStream_t);
 
 }  // namespace fa

@@ -47,9 +47,15 @@ struct BwdArgs {
   float sl2;    // scale * log2(e)
 };
 
+// Launchers per element type E (kElemBf16 = 0, kElemF16 = 1 in fa_common.hpp): the kernel
+// translation units are compiled once per element type and each defines its instance.
+template <int E>
 hipError_t launch_fwd(FwdArgs a, int d, bool causal, int mode, bool stats, bool kahan, hipStream_t s);
+template <int E>
 hipError_t launch_bwd_delta(BwdArgs a, int d, hipStream_t s);
+template <int E>
 hipError_t launch_bwd_dkdv(BwdArgs a, int d, bool causal, hipStream_t s);
+template <int E>
 hipError_t launch_bwd_dq(BwdArgs a, int d, bool causal, hipStream_t s);
 int fwd_kv_block(int d, bool causal);
 hipError_t launch_mfma_peak(float* out, int n_workgroups, int iters, hipStream_t stream);

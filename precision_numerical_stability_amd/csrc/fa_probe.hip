@@ -11,7 +11,7 @@ constexpr int kProbeThreads = 256;
 
 __global__ __launch_bounds__(kProbeThreads) void mfma_peak_kernel(float* out, int iters) {
   const int lane = threadIdx.x & 63;
-  bf16x8 a, b;
+  e16x8 a, b;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     a[i] = (__bf16)(float)((lane + i) & 3);
@@ -22,7 +22,7 @@ __global__ __launch_bounds__(kProbeThreads) void mfma_peak_kernel(float* out, in
   for (int c = 0; c < 4; ++c) acc[c] = zero16();
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int m = 0; m < 32; ++m) acc[m & 3] = mfma32x32x16(a, b, acc[m & 3]);
+    for (int m = 0; m < 32; ++m) acc[m & 3] = mfma32x32x16<kElemBf16>(a, b, acc[m & 3]);
   }
   float s = 0.f;
 #pragma unroll

@@ -198,3 +198,46 @@ def test_qk_without_a_device_reports_hip_error(lib, ffi):
     assert _fwd_qk(lib, Nq=0) == ffi.FA_OK
     assert _bwd_qk(lib, Nq=0) == ffi.FA_ERR_HIP
     assert _fwd_qk(lib, Nk=0, k=None, v=None) == ffi.FA_ERR_HIP
+
+
+def _fwd_elem(lib, elem, q=P, B=1, H=2, Nq=128, Nk=64, d=64, causal=2):
+    return lib.fa_fwd_elem(q, P, P, P, P, None, None, None, None, B, H, Nq, Nk, d, causal, 0.125, 1.25,
+                           1, 0, elem, None)
+
+
+def _bwd_elem(lib, elem, ptrs=None, B=1, H=2, Nq=128, Nk=64, d=64, causal=2, stages=7):
+    p = list(ptrs or [P] * 10)
+    return lib.fa_bwd_elem(*p, B, H, Nq, Nk, d, causal, 0.125, 1.25, 1, stages, elem, None)
+
+
+def test_elem_entry_points_validate(lib, ffi):
+    for elem in (-1, 2, 7):
+        assert _fwd_elem(lib, elem) == ffi.FA_ERR_PARAM
+        assert _bwd_elem(lib, elem) == ffi.FA_ERR_PARAM
+    for elem in (ffi.FA_ELEM_BF16, ffi.FA_ELEM_F16):
+        # the other checks run first and are the same for both element types
+        assert _fwd_elem(lib, elem, q=None) == ffi.FA_ERR_NULL
+        assert _fwd_elem(lib, elem, d=96) == ffi.FA_ERR_HEADDIM
+        assert _fwd_elem(lib, elem, causal=3) == ffi.FA_ERR_PARAM
+        assert _bwd_elem(lib, elem, [P] * 9 + [None]) == ffi.FA_ERR_NULL
+        assert _bwd_elem(lib, elem, stages=8) == ffi.FA_ERR_PARAM
+        assert _fwd_elem(lib, elem, B=0, q=None) == ffi.FA_OK
+        assert _bwd_elem(lib, elem, [None] * 10, Nq=0, Nk=0) == ffi.FA_OK
+    # the element type is checked even where nothing would run
+    assert _fwd_elem(lib, 2, B=0, q=None) == ffi.FA_ERR_PARAM
+
+
+@pytest.mark.skipif(_gpu_present(), reason="needs a host without a GPU (fake pointers would be launched)")
+def test_elem_without_a_device_reports_hip_error(lib, ffi):
+    for elem in (ffi.FA_ELEM_BF16, ffi.FA_ELEM_F16):
+        assert _fwd_elem(lib, elem) == ffi.FA_ERR_HIP
+        assert _bwd_elem(lib, elem) == ffi.FA_ERR_HIP
+
+
+def test_binding_rejects_mixed_or_unsupported_dtypes():
+    import torch
+    import precision_numerical_stability_amd as fa
+    with pytest.raises(ValueError):
+        fa._elem(torch.zeros(1, dtype=torch.float32), "q")
+    assert fa._elem(torch.zeros(1, dtype=torch.float16), "q") == fa.FA_ELEM_F16
+    assert fa._elem(torch.zeros(1, dtype=torch.bfloat16), "q") == fa.FA_ELEM_BF16
