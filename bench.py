@@ -21,7 +21,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "attention TFLOP/s fwd & fwd+bwd (bf16, % MFMA peak), N=8192 d=128 causal"
-# MI355X published peaks: dense bf16 MFMA and HBM3E bandwidth.
+# MI355X published peaks: dense bf16 (and fp16) MFMA and HBM3E bandwidth.
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
 
@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--config", type=int, default=4, help="workload id (1-5)")
     ap.add_argument("--mode", type=int, default=1, help="stable_flag: 0, 1 or 2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-f16", action="store_true",
+                    help="skip the fp16 leg (the same workload with fp16 inputs, reported beside "
+                         "the bf16 headline)")
     ap.add_argument("--kernel-iters", type=int, default=20)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (to scale HBM "
@@ -208,6 +211,38 @@ def main():
 
     ff = fwd_flops(B, H, N, d, causal)
     total = 3.5 * ff
+
+    # fp16 leg: the same draws rounded to fp16 (fa_fwd_elem / fa_bwd_elem), whole step and
+    # forward alone, after the bf16 measurements.
+    f16 = None
+    if not args.no_f16:
+        del g, q, k, v, do
+        t16 = make_inputs(cfg, dtype=torch.float16)
+        h = {k_: v_.to(dev) for k_, v_ in t16.items()}
+        o16 = torch.empty_like(h["q"])
+        dq16, dk16, dv16 = (torch.empty_like(h["q"]) for _ in range(3))
+
+        def fwd16():
+            fa.fa_fwd_elem(h["q"], h["k"], h["v"], o16, lse, None, None, None, None, int(causal),
+                           scale, 1.25, mode, stream=stream)
+
+        def step16():
+            fwd16()
+            fa.fa_bwd_elem(h["q"], h["k"], h["v"], o16, lse, h["do"], dq16, dk16, dv16, delta,
+                           int(causal), scale, stream=stream)
+
+        for _ in range(args.warmup):
+            step16()
+        torch.cuda.synchronize()
+        ms16 = time_events(step16, args.steps, stream)
+        ms16_fwd = time_events(fwd16, it, stream)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o16.float()).all() and torch.isfinite(dq16.float()).all()
+        f16 = {"ms_per_step": ms16, "fwdbwd_TFLOP/s": total / (ms16 * 1e-3) / 1e12,
+               "fwdbwd_frac_f16_peak": total / (ms16 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+               "fwd_ms": ms16_fwd, "fwd_TFLOP/s": ff / (ms16_fwd * 1e-3) / 1e12,
+               "fwd_frac_f16_peak": ff / (ms16_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        del h, o16, dq16, dk16, dv16
     value = total / (ms_step * 1e-3) / 1e12
     fwd_tf = ff / (ms_fwd * 1e-3) / 1e12
     pairs = B * H * (N * (N + 1) // 2 if causal else N * N)
@@ -272,6 +307,8 @@ def main():
         "kernels": kernels,
         "roofline": roof,
     }
+    if f16 is not None:
+        out["f16"] = f16
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, t, mode)
     print(json.dumps(out), flush=True)
