@@ -229,3 +229,33 @@ def test_f16_rejects_mixed_element_types(fa):
     k = torch.zeros((1, 1, 128, 64), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(ValueError):
         fa.forward(q, k, k, False, 0.125)
+
+
+@pytest.mark.parametrize("compensated", [False, True])
+@pytest.mark.parametrize("causal,nq,nk", [(0, 256, 256), (1, 333, 333), (2, 300, 100)])
+def test_f16_monitors_and_compensated_sum(fa, compensated, causal, nq, nk):
+    """The diagnostics variant in fp16: per-row score range (smin, smax), repeat counts and the
+    compensated row sum, against the oracle; the gradients from its LSE."""
+    _say("f16-monitor", compensated, causal, nq, nk)
+    t = rect_inputs(1, 2, nq, nk, 64, seed=1700 + nq + nk + causal, dtype=F16)
+    g = _to_dev(t)
+    scale = 0.125
+    o, lse, dup, ones, smin, smax = fa.forward(g["q"], g["k"], g["v"], causal, scale, BETA, 2,
+                                               stats=True, monitor=True,
+                                               compensated_sum=compensated)
+    dq, dk, dv = fa.backward(g["q"], g["k"], g["v"], o, lse, g["do"], causal, scale)
+    torch.cuda.synchronize()
+    res = {"o": o.float().cpu().numpy(), "lse": lse.cpu().numpy(), "dup": dup.cpu().numpy(),
+           "ones": ones.cpu().numpy(), "dq": dq.float().cpu().numpy(),
+           "dk": dk.float().cpu().numpy(), "dv": dv.float().cpu().numpy()}
+    for h in range(2):
+        fr = check16(res, t, 0, h, causal, scale, 2)
+        empty = fr.lse == -np.inf
+        got_min, got_max = smin[0, h].cpu().numpy(), smax[0, h].cpu().numpy()
+        assert np.all(got_min[empty] == np.inf) and np.all(got_max[empty] == -np.inf)
+        np.testing.assert_allclose(got_min[~empty], fr.smin[~empty], rtol=1e-5, atol=1e-5)
+        np.testing.assert_allclose(got_max[~empty], fr.rm[~empty], rtol=1e-5, atol=1e-5)
+        # Mode 2 shifts every row off its maximum, so no P^ rounds to 1.0 unless the maximum is
+        # within ~2^-12 of 0 (then e^{-(beta - 1) rm} or e^{rm} rounds to 1 in binary16).
+        away = ~empty & (np.abs(fr.rm) > 1e-2)
+        assert away.sum() > 0.9 * (~empty).sum() and np.all(res["ones"][0, h][away] == 0)
