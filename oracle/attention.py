@@ -94,7 +94,36 @@ def fp16_round(x):
     return np.where(np.abs(r) > 65504.0, np.copysign(np.inf, x), r)
 
 
-ELEM_ROUND = {"bf16": bf16_round, "f16": fp16_round}
+def e4m3_round(x):
+    """Round float64 values to the nearest OCP FP8 E4M3 value (the "e4m3fn" encoding), ties to
+    even, returned as float64.
+
+    E4M3 keeps 4 significant bits (3 stored) for normal values (|x| >= 2^-6, exponent bias 7), a
+    fixed spacing of 2^-9 below that (subnormals), and its largest finite value is 448 (the
+    encoding has no infinity).  FP8 is the lower-precision format [BF16-FA] §6.1 extends the
+    method to.  Magnitudes that round above 448 are outside what this oracle needs and come back
+    as nan.  Rounded directly from fp64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, expo = np.frexp(x)  # x = mant * 2**expo, |mant| in [0.5, 1)
+    e = np.maximum(expo, -5)  # below 2^-6 the spacing stays 2^-9 = 2^(-5 - 4)
+    r = np.ldexp(np.rint(np.ldexp(x, 4 - e)), e - 4)
+    return np.where(np.abs(r) > 448.0, np.nan, r)
+
+
+# The FP8 P^ V variant rounds P^ (at most 1) as e4m3(2^8 P^) / 2^8, so that P^ in (2^-14, 1] stays
+# in E4M3's normal range; V is rounded block by block with a scale taken from the block's largest
+# magnitude (see oracle.tiled.tiled_forward, pv="fp8").
+P_HAT_FP8_LOG2_SCALE = 8
+
+
+def fp8_p_hat_round(p):
+    """P^ as the FP8 P^ V variant feeds it to the product: e4m3(2^8 P^) / 2^8."""
+    return np.ldexp(e4m3_round(np.ldexp(np.asarray(p, dtype=np.float64), P_HAT_FP8_LOG2_SCALE)),
+                    -P_HAT_FP8_LOG2_SCALE)
+
+
+ELEM_ROUND = {"bf16": bf16_round, "f16": fp16_round, "fp8": fp8_p_hat_round}
 
 
 def scaled_scores(q_rows, k, scale, mask):

@@ -25,16 +25,38 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import ELEM_ROUND, stable_shift, visible
+from .attention import ELEM_ROUND, e4m3_round, fp8_p_hat_round, stable_shift, visible
 
 
-def tiled_forward(q, k, v, causal, scale, beta=1.25, mode=0, bc=64, order=None, elem="bf16"):
+def fp8_v_block(v_block):
+    """V of one key block as the FP8 P^ V variant feeds it to the product: with the block's
+    dynamic scale s = amax |V| / 448 (fp32 division; s = 1 for an all-zero block), each entry is
+    rounded as e4m3(fp32(v * fp32(1 / s))) and stands for that value times s.  The scale and the
+    scaled value are formed in fp32 because that is where the rounding to E4M3 is decided.
+    Returns (the dequantised block as float64, s)."""
+    vb = np.asarray(v_block, dtype=np.float64)
+    amax = np.float32(np.max(np.abs(vb))) if vb.size else np.float32(0.0)
+    s = np.float32(amax) / np.float32(448.0) if amax > 0 else np.float32(1.0)
+    inv = np.float32(1.0) / s
+    scaled = (vb.astype(np.float32) * inv).astype(np.float64)
+    return e4m3_round(scaled) * np.float64(s), float(s)
+
+
+def tiled_forward(q, k, v, causal, scale, beta=1.25, mode=0, bc=64, order=None, elem="bf16",
+                  pv="exact"):
     """Tiled forward over one head; returns dict(o, lse, r, c, m, ones).
 
     `order` lists the key-block indices in processing order (default: ascending).  Key blocks
-    entirely invisible to a row leave that row's state unchanged.  `elem` ("bf16" or "f16") is the
-    type P^ is rounded to for the exact-1.0 count.
+    entirely invisible to a row leave that row's state unchanged.  `elem` ("bf16", "f16" or "fp8")
+    is the type P^ is rounded to for the exact-1.0 count.
+
+    pv="fp8" is the FP8 P^ V variant ([BF16-FA] §6.1 names FP8 as the next lower precision): the
+    block's product P^ V takes P^ rounded by fp8_p_hat_round and V rounded by fp8_v_block (one
+    dynamic scale per key block of width bc); the row sum l, the shift m and the LSE are the
+    unrounded ones, and O = acc / l as before.
     """
+    if pv not in ("exact", "fp8"):
+        raise ValueError(f"pv must be 'exact' or 'fp8', got {pv!r}")
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -66,7 +88,10 @@ def tiled_forward(q, k, v, causal, scale, beta=1.25, mode=0, bc=64, order=None, 
         alpha = np.where(np.isfinite(m), np.exp(np.where(np.isfinite(m), m, 0.0) - np.where(live, m_new, 0.0)), 0.0)
         p_hat = np.where(mask, np.exp(s - np.where(live, m_new, 0.0)[:, None]), 0.0)
         l = alpha * l + p_hat.sum(axis=1)
-        acc = alpha[:, None] * acc + p_hat @ v[k0:k1]
+        if pv == "fp8":
+            acc = alpha[:, None] * acc + fp8_p_hat_round(p_hat) @ fp8_v_block(v[k0:k1])[0]
+        else:
+            acc = alpha[:, None] * acc + p_hat @ v[k0:k1]
         ones += np.sum((ELEM_ROUND[elem](p_hat) == 1.0) & mask, axis=1)
         m = m_new
     # A row with no visible key keeps l = 0: O = 0 and LSE = -inf.

@@ -711,3 +711,97 @@ def test_visible_pairs_closed_forms():
             assert oracle.visible_pairs(nq, nk, 1) == nk * (nk + 1) // 2 + (nq - nk) * nk
             assert oracle.visible_pairs(nq, nk, 2) == nk * (nk + 1) // 2
     assert oracle.visible_pairs(8192, 8192, 1) == oracle.exact_causal_pairs(8192)
+
+
+# ---- FP8 P^ V variant ---------------------------------------------------------------------------
+
+
+def _torch_e4m3(x):
+    """Round through torch's float8_e4m3fn cast (an independent implementation of the format)."""
+    import torch
+    t = torch.tensor(np.asarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_e4m3_round_matches_torch_cast_and_closed_forms():
+    rng = np.random.default_rng(8)
+    mags = np.exp2(rng.uniform(-12.0, np.log2(440.0), 200000))
+    x = (mags * rng.choice([-1.0, 1.0], mags.size)).astype(np.float32).astype(np.float64)
+    # exact midpoints between neighbours, in every normal binade up to 256 and in the subnormals
+    ties = [(np.arange(0, 8) + 0.5) * 2.0**-9]
+    ties += [(np.arange(8, 16) + 0.5) * 2.0**(e - 3) for e in range(-6, 8)]
+    x = np.concatenate([x, *ties, -np.concatenate(ties), [0.0, 448.0, -448.0, 2.0**-9, 2.0**-6]])
+    assert np.array_equal(oracle.e4m3_round(x), _torch_e4m3(x))
+    # closed forms: 4 significant bits, ties to even, 2^-9 subnormal spacing, 448 the largest value
+    assert oracle.e4m3_round(1.0625) == 1.0 and oracle.e4m3_round(1.1875) == 1.25
+    assert oracle.e4m3_round(2.0**-10) == 0.0 and oracle.e4m3_round(3 * 2.0**-10) == 2.0**-8
+    assert oracle.e4m3_round(448.0) == 448.0 and np.isnan(oracle.e4m3_round(500.0))
+    assert oracle.e4m3_round(252.0) == 256.0 and oracle.e4m3_round(247.0) == 240.0
+
+
+def test_fp8_p_hat_rounding_and_exact_one():
+    # P^ is fed as e4m3(256 P^) / 256: the spacing just below 1 is 1/16, so P^ >= 0.96875 gives 1.0
+    assert oracle.fp8_p_hat_round(1.0) == 1.0 and oracle.fp8_p_hat_round(0.97) == 1.0
+    assert oracle.fp8_p_hat_round(0.968) == 0.9375
+    # small probabilities keep 4 significant bits down to 2^-14, then the 2^-17 subnormal spacing
+    assert oracle.fp8_p_hat_round(2.0**-14 * 1.0625) == 2.0**-14
+    assert oracle.fp8_p_hat_round(2.0**-18) == 0.0 and oracle.fp8_p_hat_round(3 * 2.0**-18) == 2.0**-16
+
+
+def _brute_fp8_forward(q, k, v, causal, scale):
+    """Scalar loops, mode 0, one key block: the FP8 P^ V definition written out, with torch's cast
+    as the rounding routine."""
+    n, nk = q.shape[0], k.shape[0]
+    amax = np.float32(max(abs(float(x)) for x in v.ravel()))
+    s = amax / np.float32(448.0) if amax > 0 else np.float32(1.0)
+    inv = np.float32(1.0) / s
+    vq = np.array([[float(_torch_e4m3(np.float32(float(v[j, c])) * inv)) * float(s) for c in range(v.shape[1])]
+                   for j in range(nk)])
+    o = np.zeros((n, v.shape[1]))
+    for i in range(n):
+        keys = [j for j in range(nk) if (not causal) or j <= i]
+        sc = [scale * sum(float(q[i, t]) * float(k[j, t]) for t in range(q.shape[1])) for j in keys]
+        m = max(sc)
+        p = [math.exp(x - m) for x in sc]
+        l = sum(p)
+        for idx, j in enumerate(keys):
+            pq = float(_torch_e4m3(np.float32(256.0 * p[idx]))) / 256.0
+            o[i] += pq * vq[j] / l
+    return o
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_pv_tiled_forward_brute_force(causal):
+    rng = np.random.default_rng(81 + int(causal))
+    n, d = 12, 8
+    q = oracle.bf16_round(rng.standard_normal((n, d)))
+    k = oracle.bf16_round(rng.standard_normal((n, d)))
+    v = oracle.bf16_round(rng.standard_normal((n, d)))
+    got = oracle.tiled_forward(q, k, v, causal, 0.35, mode=0, bc=128, pv="fp8")["o"]
+    want = _brute_fp8_forward(q, k, v, causal, 0.35)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_fp8_pv_forward_within_rounding_bound(mode):
+    """Quantised against exact, per element: |O_q - O| <= sum_j P_j |v_j| (2^-4 + 2^-4 + 2^-8)
+    + 2^-14 max|v| (relative rounding of P^ and of V, their product, and the subnormal floors of
+    P^ and of V / s), with LSE unchanged."""
+    rng = np.random.default_rng(90 + mode)
+    n, d, bc = 300, 64, 128
+    q = oracle.bf16_round(rng.standard_normal((n, d)))
+    k = oracle.bf16_round(rng.standard_normal((n, d)))
+    v = oracle.bf16_round(rng.standard_normal((n, d)) * np.linspace(0.1, 3.0, n)[:, None])
+    for causal in (False, True):
+        ex = oracle.tiled_forward(q, k, v, causal, d ** -0.5, mode=mode, bc=bc)
+        f8 = oracle.tiled_forward(q, k, v, causal, d ** -0.5, mode=mode, bc=bc, pv="fp8")
+        assert np.array_equal(ex["lse"], f8["lse"])
+        fr = oracle.forward(q, k, v, causal, d ** -0.5)
+        mask = oracle.visible(np.arange(n), n, causal, n)
+        p = oracle.probabilities(q, k, d ** -0.5, fr.lse, mask)
+        weight = p @ np.abs(v)
+        bound = weight * (2.0**-4 + 2.0**-4 + 2.0**-8) + 2.0**-14 * np.abs(v).max()
+        err = np.abs(f8["o"] - ex["o"])
+        assert np.all(err <= bound), (err - bound).max()
+        assert err.max() > 1e-4  # the rounding is really there
+        assert np.allclose(ex["o"], fr.o, rtol=1e-12, atol=1e-12)
