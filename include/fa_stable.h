@@ -190,6 +190,30 @@ int fa_bwd_elem(const void* q, const void* k, const void* v, const void* o, cons
                 int B, int H, int Nq, int Nk, int d, int causal, float scale, float beta,
                 int stable_flag, int stages, int elem, void* stream);
 
+/* Forward pass with the P^ V product in FP8 (OCP E4M3, the "e4m3fn" encoding, largest value 448):
+ * the lower-precision extension the ijyty.com article §6.1 names, with dynamic scaling.  Tensors,
+ * shapes, diagnostics, causal alignments and errors as fa_fwd_qk (bf16 q, k, v, o); the scores
+ * Q K^T, the softmax statistics, l and lse stay as in the bf16 forward.  Only the operands of the
+ * P^ V product are rounded to E4M3 (round to nearest even):
+ *   - V, per head and block of 128 consecutive keys: s = amax |V_block| / 448 (fp32; s = 1 for an
+ *     all-zero block), each value stored as E4M3(v * (1 / s)) and standing for that value times s;
+ *   - P^ = exp(S - m) <= 1, as E4M3(2^8 P^) (so that P^ down to 2^-14 keeps 4 significant bits),
+ *     standing for that value times 2^-8.
+ * O = sum over blocks of the rescaled products, divided by the unrounded l.  ones counts the P^
+ * whose rounded value is exactly 1.0 (2^8 P^ rounds to 256, i.e. P^ >= 0.96875).  The key blocks
+ * of this forward are 128 keys wide whether or not it is causal.
+ * workspace: caller-owned device memory of fa_fwd_fp8pv_workspace_bytes(B, H, Nk, d) bytes, 16-byte
+ * aligned (may be NULL when Nk == 0); the call overwrites it with the E4M3 V blocks and their
+ * scales, so concurrent calls need separate workspaces.  Two kernels run in order on the stream.
+ * The backward of this forward is fa_bwd_qk (it rebuilds P from lse, which is unrounded). */
+int fa_fwd_fp8pv(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int32_t* dupcnt, int32_t* ones, float* smin, float* smax, void* workspace,
+                 int B, int H, int Nq, int Nk, int d, int causal, float scale, float beta,
+                 int stable_flag, int flags, void* stream);
+
+/* Bytes of the fa_fwd_fp8pv workspace: B*H*ceil(Nk/128)*(d*128 + 4) (0 for invalid shapes). */
+size_t fa_fwd_fp8pv_workspace_bytes(int B, int H, int Nk, int d);
+
 /* Bytes of the delta workspace fa_bwd needs: B*H*N*4 (0 for invalid or empty shapes); for
  * fa_bwd_qk pass N = Nq. */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);

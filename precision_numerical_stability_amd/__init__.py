@@ -38,6 +38,7 @@ DEFAULT_BETA = 1.25
 __all__ = [
     "fa_fwd", "fa_fwd_ex", "fa_fwd_stats", "fa_fwd_qk", "fa_fwd_elem", "FA_FWD_COMPENSATED_SUM",
     "fa_bwd", "fa_bwd_ex", "fa_bwd_qk", "fa_bwd_elem", "FA_ELEM_BF16", "FA_ELEM_F16",
+    "fa_fwd_fp8pv", "fa_fwd_fp8pv_workspace_bytes", "forward_fp8pv",
     "fa_bwd_workspace_bytes", "fa_fwd_kv_block", "fa_probe_mfma_peak",
     "FA_CAUSAL_NONE", "FA_CAUSAL_TOP_LEFT", "FA_CAUSAL_BOTTOM_RIGHT", "fa_status_str",
     "fa_last_hip_error", "FaError", "forward", "backward", "attention", "STANDARD", "TIE_RULE",
@@ -198,6 +199,33 @@ def fa_fwd_elem(q, k, v, o, lse, dupcnt, ones, smin, smax, causal, scale, beta, 
     _raise(st)
 
 
+def fa_fwd_fp8pv_workspace_bytes(B: int, H: int, Nk: int, d: int) -> int:
+    return int(_lib.fa_fwd_fp8pv_workspace_bytes(B, H, Nk, d))
+
+
+def fa_fwd_fp8pv(q, k, v, o, lse, dupcnt, ones, smin, smax, workspace, causal, scale, beta,
+                 stable_flag, flags=0, stream=None):
+    """Call fa_fwd_fp8pv on torch tensors: as fa_fwd_qk (bf16), plus `workspace`, a uint8 CUDA
+    tensor of at least fa_fwd_fp8pv_workspace_bytes(B, H, Nk, d) bytes."""
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    for name, t, n in (("q", q, Nq), ("o", o, Nq), ("k", k, Nk), ("v", v, Nk)):
+        _check(t, name, torch.bfloat16, (B, H, n, d))
+    _check(lse, "lse", torch.float32, (B, H, Nq))
+    for name, t, dt in (("dupcnt", dupcnt, torch.int32), ("ones", ones, torch.int32),
+                        ("smin", smin, torch.float32), ("smax", smax, torch.float32)):
+        if t is not None:
+            _check(t, name, dt, (B, H, Nq))
+    need = fa_fwd_fp8pv_workspace_bytes(B, H, Nk, d)
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda or workspace.numel() < need:
+        raise ValueError(f"workspace must be a uint8 CUDA tensor of at least {need} bytes")
+    st = _lib.fa_fwd_fp8pv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dupcnt), _ptr(ones),
+                           _ptr(smin), _ptr(smax), _ptr(workspace), B, H, Nq, Nk, d, int(causal),
+                           float(scale), float(beta), int(stable_flag), int(flags),
+                           _stream_handle(q.device, stream))
+    _raise(st)
+
+
 def fa_fwd(q, k, v, o, lse, causal, scale, beta, stable_flag, stream=None):
     fa_fwd_ex(q, k, v, o, lse, None, None, causal, scale, beta, stable_flag, stream)
 
@@ -295,6 +323,34 @@ def forward(q, k, v, causal=False, scale=None, beta=DEFAULT_BETA, stable_flag=TI
     flags = FA_FWD_COMPENSATED_SUM if compensated_sum else 0
     fa_fwd_elem(q, k, v, o, lse, dup, ones, smin, smax, int(causal), scale, beta, stable_flag, flags,
                 stream)
+    out = (o, lse)
+    if stats:
+        out += (dup, ones)
+    if monitor:
+        out += (smin, smax)
+    return out
+
+
+def forward_fp8pv(q, k, v, causal=False, scale=None, beta=DEFAULT_BETA, stable_flag=TIE_RULE,
+                  stats=False, monitor=False, compensated_sum=False, stream=None):
+    """As forward() for bf16 tensors, with the P^ V product in FP8 (fa_fwd_fp8pv); allocates the
+    workspace with torch."""
+    B, H, N, d = q.shape
+    scale = _default_scale(d) if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    ws = torch.empty(max(1, fa_fwd_fp8pv_workspace_bytes(B, H, k.shape[2], d)), dtype=torch.uint8,
+                     device=q.device)
+    dup = ones = smin = smax = None
+    if stats:
+        dup = torch.empty((B, H, N), dtype=torch.int32, device=q.device)
+        ones = torch.empty((B, H, N), dtype=torch.int32, device=q.device)
+    if monitor:
+        smin = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        smax = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    flags = FA_FWD_COMPENSATED_SUM if compensated_sum else 0
+    fa_fwd_fp8pv(q, k, v, o, lse, dup, ones, smin, smax, ws, int(causal), scale, beta, stable_flag,
+                 flags, stream)
     out = (o, lse)
     if stats:
         out += (dup, ones)

@@ -46,6 +46,8 @@ SIGNATURES = {
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _I, _P]),
     "fa_bwd_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _I, _I, _P]),
     "fa_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "fa_fwd_fp8pv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _I, _P]),
+    "fa_fwd_fp8pv_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "fa_fwd_kv_block": (_I, [_I, _I]),
     "fa_probe_mfma_peak": (_I, [_P, _I, _I, _P]),
     "fa_status_str": (ctypes.c_char_p, [_I]),

@@ -16,10 +16,12 @@ CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "_lib")
 LIBNAME = "libfa_stable.so"
 # (source, object name, extra defines).  The kernel files are compiled once per element type:
-# FA_ELEM=0 instantiates the bf16 kernels, FA_ELEM=1 the fp16 ones.
+# FA_ELEM=0 instantiates the bf16 kernels, FA_ELEM=1 the fp16 ones, FA_ELEM=2 (forward only)
+# the bf16 forward with an FP8 P^ V product and its V quantisation kernel.
 UNITS = (
     ("fa_fwd.hip", "fa_fwd_bf16", ("-DFA_ELEM=0",)),
     ("fa_fwd.hip", "fa_fwd_f16", ("-DFA_ELEM=1",)),
+    ("fa_fwd.hip", "fa_fwd_fp8pv", ("-DFA_ELEM=2",)),
     ("fa_bwd.hip", "fa_bwd_bf16", ("-DFA_ELEM=0",)),
     ("fa_bwd.hip", "fa_bwd_f16", ("-DFA_ELEM=1",)),
     ("fa_api.cpp", "fa_api", ()),

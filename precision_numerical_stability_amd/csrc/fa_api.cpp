@@ -45,23 +45,28 @@ int hip_status(hipError_t e) {
   return FA_ERR_HIP;
 }
 
-}  // namespace
+// Bytes of the FP8 P^ V workspace: E4M3 V blocks (d rows of 128 bytes per 128-key block and head),
+// then one fp32 scale per block and head.
+size_t fp8pv_v8_bytes(int64_t bh, int Nk, int d) { return size_t(bh) * size_t((Nk + 127) / 128) * size_t(d) * 128; }
 
-extern "C" {
-
-int fa_fwd_elem(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* dupcnt,
-                int32_t* ones, float* smin, float* smax, int B, int H, int Nq, int Nk, int d, int causal,
-                float scale, float beta, int stable_flag, int flags, int elem, void* stream) {
+// The forward entry points share this body; elem is FA_ELEM_BF16, FA_ELEM_F16 or -1 for the FP8
+// P^ V variant (bf16 tensors), which also takes the workspace.
+int fwd_body(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* dupcnt, int32_t* ones,
+             float* smin, float* smax, void* workspace, int B, int H, int Nq, int Nk, int d, int causal,
+             float scale, float beta, int stable_flag, int flags, int elem, void* stream) {
+  const bool fp8pv = elem < 0;
   const int st = check_common(B, H, Nq, Nk, d, causal, scale, beta, stable_flag);
   if (st != FA_OK) return st;
   if ((flags & ~FA_FWD_COMPENSATED_SUM) != 0) return FA_ERR_PARAM;
-  if (elem != FA_ELEM_BF16 && elem != FA_ELEM_F16) return FA_ERR_PARAM;
+  if (!fp8pv && elem != FA_ELEM_BF16 && elem != FA_ELEM_F16) return FA_ERR_PARAM;
   if (int64_t(B) * H == 0 || Nq == 0) return FA_OK;
   if (!q || !o || !lse) return FA_ERR_NULL;
   if (Nk > 0 && (!k || !v)) return FA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return FA_ERR_ALIGN;
   if (!aligned(lse, 4) || (dupcnt && !aligned(dupcnt, 4)) || (ones && !aligned(ones, 4))) return FA_ERR_ALIGN;
   if ((smin && !aligned(smin, 4)) || (smax && !aligned(smax, 4))) return FA_ERR_ALIGN;
+  if (fp8pv && Nk > 0 && !workspace) return FA_ERR_NULL;
+  if (fp8pv && !aligned(workspace, 16)) return FA_ERR_ALIGN;
 
   fa::FwdArgs a{};
   a.q = static_cast<const uint16_t*>(q);
@@ -83,8 +88,48 @@ int fa_fwd_elem(const void* q, const void* k, const void* v, void* o, float* lse
   const bool stats = dupcnt || ones || smin || smax;
   const bool kahan = (flags & FA_FWD_COMPENSATED_SUM) != 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fp8pv) {
+    const int64_t bh = int64_t(B) * H;
+    a.n_vblk = (Nk + 127) / 128;
+    a.v8 = static_cast<const uint8_t*>(workspace);
+    a.vscale = reinterpret_cast<const float*>(static_cast<const uint8_t*>(workspace) + fp8pv_v8_bytes(bh, Nk, d));
+    uint8_t* v8 = static_cast<uint8_t*>(workspace);
+    float* vscale = reinterpret_cast<float*>(v8 + fp8pv_v8_bytes(bh, Nk, d));
+    const int rc = hip_status(fa::launch_v8_pack(a.v, v8, vscale, B * H, Nk, d, s));
+    if (rc != FA_OK) return rc;
+    return hip_status(fa::launch_fwd<fa::kElemFp8PV>(a, d, causal != 0, stable_flag, stats, kahan, s));
+  }
   return hip_status(elem == FA_ELEM_F16 ? fa::launch_fwd<fa::kElemF16>(a, d, causal != 0, stable_flag, stats, kahan, s)
                                         : fa::launch_fwd<fa::kElemBf16>(a, d, causal != 0, stable_flag, stats, kahan, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd_elem(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* dupcnt,
+                int32_t* ones, float* smin, float* smax, int B, int H, int Nq, int Nk, int d, int causal,
+                float scale, float beta, int stable_flag, int flags, int elem, void* stream) {
+  if (elem != FA_ELEM_BF16 && elem != FA_ELEM_F16) {
+    // parameters are checked in the documented order: shapes and scalars first
+    const int st = check_common(B, H, Nq, Nk, d, causal, scale, beta, stable_flag);
+    return st != FA_OK ? st : FA_ERR_PARAM;
+  }
+  return fwd_body(q, k, v, o, lse, dupcnt, ones, smin, smax, nullptr, B, H, Nq, Nk, d, causal, scale, beta,
+                  stable_flag, flags, elem, stream);
+}
+
+size_t fa_fwd_fp8pv_workspace_bytes(int B, int H, int Nk, int d) {
+  if (B < 0 || H < 0 || Nk < 0 || (d != 64 && d != 128)) return 0;
+  const int64_t bh = int64_t(B) * H;
+  return fp8pv_v8_bytes(bh, Nk, d) + size_t(bh) * size_t((Nk + 127) / 128) * sizeof(float);
+}
+
+int fa_fwd_fp8pv(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* dupcnt,
+                 int32_t* ones, float* smin, float* smax, void* workspace, int B, int H, int Nq, int Nk, int d,
+                 int causal, float scale, float beta, int stable_flag, int flags, void* stream) {
+  return fwd_body(q, k, v, o, lse, dupcnt, ones, smin, smax, workspace, B, H, Nq, Nk, d, causal, scale, beta,
+                  stable_flag, flags, -1, stream);
 }
 
 int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* dupcnt,

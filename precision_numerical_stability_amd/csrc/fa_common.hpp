@@ -46,6 +46,10 @@ constexpr float kLn2 = 0.6931471805599453f;
 // (P^ and dS are rounded to it too).  Arithmetic is fp32 for both.
 constexpr int kElemBf16 = 0;
 constexpr int kElemF16 = 1;
+// bf16 tensors, with the P^ V product of the forward in FP8 (OCP E4M3): P^ rounded as
+// e4m3(2^8 P^), V pre-rounded per 128-key block with a dynamic scale (v8_pack_kernel).  Every
+// other product and every stored tensor is bf16, so the bf16 paths below serve it unchanged.
+constexpr int kElemFp8PV = 2;
 
 // Bit pattern of 1.0 in the element type.
 template <int E>
@@ -68,6 +72,23 @@ __device__ __forceinline__ f32x16 zero16() {
   for (int i = 0; i < 16; ++i) z[i] = 0.f;
   return z;
 }
+
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+
+// C += A B, 32 x 32 x 64, fp32 accumulation, E4M3 operands (32 bytes per lane: lanes 0-31 and
+// 32-63 each hold one half of the k range).  A and B pair up by (lane half, byte slot), so the
+// kernels may place the k values in any order that both operands share.  Unit block scales.
+__device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Four fp32 -> four E4M3 bytes (round to nearest even), byte t = value t.
+__device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+constexpr uint32_t kFp8OneX256 = 0x78;  // E4M3 encoding of 256 = 2^8 x 1.0
 
 // Two fp32 -> a packed pair of the element type (round to nearest even; fp16 overflows to inf),
 // low half = a.
@@ -216,6 +237,18 @@ struct DirectStage {
       const int pc = p % kChunksPerRow;
       voff[i] = r * (D * 2) + ((pc ^ swz<D>(r)) << 4);
     }
+  }
+  // As issue, with this lane's offsets formed on the spot instead of read from voff (for kernels
+  // short of registers); needs only `wave` set.
+  __device__ __forceinline__ void issue_lazy(const uint16_t* head, int row0, int n_rows, uint32_t lds, int lane) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int p = (wave * kPer + i) * 64 + lane;
+      const int r = p / kChunksPerRow;
+      const int pc = p % kChunksPerRow;
+      voff[i] = r * (D * 2) + ((pc ^ swz<D>(r)) << 4);
+    }
+    issue(head, row0, n_rows, lds);
   }
   // lds: byte address of the destination tile in LDS (lds_addr of the __shared__ array).
   __device__ __forceinline__ void issue(const uint16_t* head, int row0, int n_rows, uint32_t lds) const {

@@ -36,9 +36,11 @@
 
 namespace fa {
 
-// Keys per block: 128 when causal; 64 otherwise (the non-causal instances spill at 128).
-template <bool CAUSAL>
-constexpr int fwd_bc() { return CAUSAL ? 128 : 64; }
+// Keys per block: 128 when causal; 64 otherwise (the non-causal instances spill at 128).  The
+// FP8 P^ V instances always take 128 (their P^ packs into half the registers, and V arrives in
+// 128-key blocks, each with its own scale).
+template <int E, bool CAUSAL>
+constexpr int fwd_bc() { return (CAUSAL || E == kElemFp8PV) ? 128 : 64; }
 constexpr int kFwdBr = 256;  // queries per workgroup
 constexpr int kFwdThreads = 512;
 
@@ -52,11 +54,14 @@ struct RowState {
   float lcomp;    // its compensation term (compensated-sum variant): lost low-order part, negated
   float run_min;  // running min of the raw dot products over visible keys (diagnostics variant)
   int n_ones;     // exact-1.0 16-bit P^ values seen (stats variant)
+  float vs;       // FP8 P^ V: scale of the V block last added (O is held in units of vs / 2^8)
 };
 
 template <int E, int D, bool CAUSAL, int MODE, bool STATS, bool KAHAN>
 __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
-  constexpr int BC = fwd_bc<CAUSAL>(), BR = kFwdBr, KS = D / 16, DT = D / 32, KB = BC / 32;
+  constexpr int BC = fwd_bc<E, CAUSAL>(), BR = kFwdBr, KS = D / 16, DT = D / 32, KB = BC / 32;
+  constexpr bool FP8 = (E == kElemFp8PV);
+  static_assert(!FP8 || BC == 128, "the FP8 V blocks hold 128 keys");
   // Mode 1 needs only whether the running maximum repeats: without the diagnostics that is
   // decided by tracking the two largest scores; the diagnostics need the exact count.
   constexpr bool TOP2 = (MODE == 1) && !STATS;
@@ -103,12 +108,21 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = zero16();
-  RowState rs{-INFINITY, 0, -INFINITY, -INFINITY, 0.f, 0.f, INFINITY, 0};
+  RowState rs{-INFINITY, 0, -INFINITY, -INFINITY, 0.f, 0.f, INFINITY, 0, 1.f};
   f32x16 s[KB];
   uint32_t pk[KB][8];
+  // FP8: P^ of 64-key chunk c packed as one 8-register tuple (the MFMA's B operand): dwords 0-3
+  // from 32-key sub-block 2 c, dwords 4-7 from sub-block 2 c + 1.
+  i32x8 pk8[FP8 ? KB / 2 : 1];
 
   DirectStage<BC, D, kFwdThreads / 2> stg;  // group A's threads stage every tile
   stg.init(tid & (kFwdThreads / 2 - 1));
+  // FP8 P^ V: the V block is D rows (one per head dimension) of 128 E4M3 bytes, staged like a
+  // D x 64 tile of 16-bit elements.
+  DirectStage<D, 64, kFwdThreads / 2> stg8;  // offsets formed at issue (no registers held)
+  if constexpr (FP8) stg8.wave = __builtin_amdgcn_readfirstlane((tid & (kFwdThreads / 2 - 1)) >> 6);
+  const uint16_t* V8g = FP8 ? reinterpret_cast<const uint16_t*>(a.v8 + (int64_t)bh * a.n_vblk * (D * 128)) : nullptr;
+  const float* VSg = FP8 ? a.vscale + (int64_t)bh * a.n_vblk : nullptr;
   constexpr uint32_t kTileBytes = BC * D * 2;
   const uint32_t aK = lds_addr(&sK[0][0]), aV = lds_addr(&sV[0][0]);
   if (grp == 0) stg.issue(Kg, 0, Nk, aK);
@@ -123,24 +137,70 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   // block.  The LDS operand of step k + MDEPTH is read at step k into a register ring; the
   // rescale of O by the previous block's alpha runs beside the MFMAs (d-tile 0 before the first
   // step, d-tile t + 1 during the steps of d-tile t; alpha == 1 leaves O unchanged).
-  constexpr int KK = BC / 16;
+  // FP8: a d-tile takes BC / 64 MFMAs of k = 64, each fed by two 16-byte reads (two steps: the
+  // first only reads, the second reads and multiplies).
+  constexpr int KK = FP8 ? 2 * (BC / 64) : BC / 16;
   constexpr int NPV = DT * KK, NSS = KB * KS;
-  constexpr int MDEPTH = 4, MRING = MDEPTH + 1;
+  constexpr int MDEPTH = FP8 ? 3 : 4, MRING = MDEPTH + 1;
   e16x8 mring[MRING];
+  // FP8 instances: step k's operand is half k & 1 of mring8[(k / 2) % 3], so the two 16-byte
+  // reads of one k = 64 MFMA fill one 8-register tuple.  At step k the MFMA still uses step k - 1's
+  // half while the read for step k + MDEPTH is issued: MDEPTH + 2 steps in flight, 6 positions.
+  constexpr int R8 = 3;
+  static_assert(!FP8 || 2 * R8 >= MDEPTH + 2, "ring positions must cover the steps in flight");
+  i32x8 mring8[R8];
+  auto ring_put = [&](auto kc, e16x8 x) __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
+    if constexpr (FP8) {
+      const i32x4 h = __builtin_bit_cast(i32x4, x);
+      i32x8& slot = mring8[(k >> 1) % R8];
+      if constexpr (k & 1)
+        slot = __builtin_shufflevector(slot, __builtin_shufflevector(h, h, 0, 1, 2, 3, -1, -1, -1, -1), 0, 1, 2, 3, 8, 9, 10, 11);
+      else
+        slot = __builtin_shufflevector(slot, __builtin_shufflevector(h, h, 0, 1, 2, 3, -1, -1, -1, -1), 8, 9, 10, 11, 4, 5, 6, 7);
+    } else {
+      mring[k % MRING] = x;
+    }
+  };
+  auto ring_get = [&](auto kc) __attribute__((always_inline)) -> e16x8 {
+    constexpr int k = decltype(kc)::value;
+    if constexpr (FP8) {
+      const i32x8 slot = mring8[(k >> 1) % R8];
+      if constexpr (k & 1)
+        return __builtin_bit_cast(e16x8, __builtin_shufflevector(slot, slot, 4, 5, 6, 7));
+      else
+        return __builtin_bit_cast(e16x8, __builtin_shufflevector(slot, slot, 0, 1, 2, 3));
+    } else {
+      return mring[k % MRING];
+    }
+  };
   auto m_read = [&](auto kc, const uint16_t* tV, const uint16_t* tK) __attribute__((always_inline)) {
     constexpr int k = decltype(kc)::value;
-    if constexpr (k < NPV) {
+    if constexpr (k < NPV && FP8) {
+      // Row 32 dt + l32 of the V block, bytes 64 ck + 32 hh + 16 part: the 32 keys of this lane
+      // half, in the order P^ sits in its accumulator registers (v8_pack_kernel writes them so).
+      constexpr int dt = k / KK, kk = k % KK, ck = kk >> 1, part = kk & 1;
+      ring_put(kc, lds_read_row8<64>(tV, 32 * dt + l32, 32 * ck + 16 * hh + 8 * part));
+    } else if constexpr (k < NPV) {
       constexpr int dt = k / KK, kk = k % KK;
-      mring[k % MRING] = lds_read_col8_tr<D>(tV, 16 * kk, 32 * dt, lane);
+      ring_put(kc, lds_read_col8_tr<D>(tV, 16 * kk, 32 * dt, lane));
     } else {
       constexpr int i = k - NPV, kb = i / KS, ks = i % KS;
-      mring[k % MRING] = lds_read_row8<D>(tK, 32 * kb + l32, 16 * ks + 8 * hh);
+      ring_put(kc, lds_read_row8<D>(tK, 32 * kb + l32, 16 * ks + 8 * hh));
     }
   };
   auto m_step = [&](auto kc) __attribute__((always_inline)) {
     constexpr int k = decltype(kc)::value;
-    const e16x8 op = mring[k % MRING];
-    if constexpr (k < NPV) {
+    if constexpr (k < NPV && FP8) {
+      constexpr int dt = k / KK, kk = k % KK, ck = kk >> 1;
+      if constexpr (kk & 1) oacc[dt] = mfma32x32x64_fp8(mring8[(k >> 1) % R8], pk8[ck], oacc[dt]);
+      if constexpr (dt + 1 < DT) {
+        constexpr int per = 16 / KK;
+#pragma unroll
+        for (int r = per * kk; r < per * (kk + 1); ++r) oacc[dt + 1][r] *= alpha_pending;
+      }
+    } else if constexpr (k < NPV) {
+      const e16x8 op = ring_get(kc);
       constexpr int dt = k / KK, kk = k % KK, o4 = (kk & 1) * 4;
       oacc[dt] = mfma32x32x16<E>(op, make_e16x8(pk[kk >> 1][o4], pk[kk >> 1][o4 + 1], pk[kk >> 1][o4 + 2],
                                               pk[kk >> 1][o4 + 3]), oacc[dt]);
@@ -150,6 +210,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
         for (int r = per * kk; r < per * (kk + 1); ++r) oacc[dt + 1][r] *= alpha_pending;
       }
     } else {
+      const e16x8 op = ring_get(kc);
       constexpr int i = k - NPV, kb = i / KS, ks = i % KS;
       s[kb] = mfma32x32x16<E>(op, qf[ks], ks == 0 ? zero16() : s[kb]);
     }
@@ -279,8 +340,36 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
     }
     const float alpha = fast_exp2(rs.m2 - m2_new);
     rs.m2 = m2_new;
+    // The factor O is rescaled by.  FP8: O is held in units of this block's V scale over 2^8, so
+    // it also takes the previous block's scale over this one's (block 0 starts from O = 0 and
+    // rs.vs = 1); the row sum l takes alpha alone.
+    float oscale = alpha;
+    if constexpr (FP8) {
+      const float vs = VSg[j];
+      oscale = alpha * (rs.vs / vs);
+      rs.vs = vs;
+    }
+    // FP8: P^ is formed as 2^8 P^ (exponent offset folded into the FMA) for its E4M3 rounding;
+    // the row sum then carries the same factor, removed in the epilogue.
+    const float m2_sub = FP8 ? m2_new - 8.f : m2_new;
     // P^ = exp2(S * scale * log2e - m), its row sum, and its 16-bit packing for the V product.
     float psum = 0.f;
+    if constexpr (FP8) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          float p[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) p[u] = fast_exp2(fmaf(s[kb][r + u], a.sl2, -m2_sub));
+          psum += (p[0] + p[1]) + (p[2] + p[3]);
+          const uint32_t w = pack4_fp8(p[0], p[1], p[2], p[3]);
+          pk8[kb >> 1][4 * (kb & 1) + (r >> 2)] = (int)w;
+          if (STATS)
+            rs.n_ones += ((w & 0xFFu) == kFp8OneX256) + (((w >> 8) & 0xFFu) == kFp8OneX256) +
+                         (((w >> 16) & 0xFFu) == kFp8OneX256) + ((w >> 24) == kFp8OneX256);
+        }
+    } else {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -292,6 +381,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
         pk[kb][r >> 1] = w;
         if (STATS) rs.n_ones += ((w & 0xFFFFu) == elem_one<E>()) + ((w >> 16) == elem_one<E>());
       }
+    }
     if constexpr (KAHAN) {
       // Compensated running sum: the previous sum and its compensation scale by alpha together;
       // the low-order part lost in adding this block's sum is kept (negated) in lcomp.
@@ -305,7 +395,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
     }
     // O is rescaled by alpha at the start of the next matrix phase, before this block is added
     // (alpha == 1 exactly changes nothing, so a wave where no lane's shift moved skips it).
-    alpha_pending = alpha;
+    alpha_pending = oscale;
   };
 
   // Both groups run the same sequence M(0) V(0) M(1) V(1) ... M(n_kv), each phase closed by a
@@ -320,7 +410,11 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
     if (grp == 0 && j + 1 < n_kv) stg.issue(Kg, (j + 1) * BC, Nk, aK + (PAR ^ 1) * kTileBytes);
     matrix_phase(j, par_tag);
     __syncthreads();
-    if (grp == 0 && j < n_kv) stg.issue(Vg, j * BC, Nk, aV + PAR * kTileBytes);
+    if constexpr (FP8) {
+      if (grp == 0 && j < n_kv) stg8.issue_lazy(V8g, j * D, a.n_vblk * D, aV + PAR * kTileBytes, lane);
+    } else {
+      if (grp == 0 && j < n_kv) stg.issue(Vg, j * BC, Nk, aV + PAR * kTileBytes);
+    }
     vector_phase(j);
     if (grp == 0) wait_vm0();
     __syncthreads();
@@ -345,7 +439,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
     // keys) has the empty sum: O = 0 and LSE = -inf.  Its lanes ran with an infinite max, so their
     // accumulators are not used.
     const bool empty = (Nk == 0) || (CAUSAL && qrow + a.coff < 0);
-    const float inv = empty ? 0.f : 1.f / ltot;
+    // FP8: ltot is 2^8 l and O is held in units of vs / 2^8, so O = oacc vs / ltot.
+    const float inv = empty ? 0.f : (FP8 ? rs.vs / ltot : 1.f / ltot);
     uint16_t* orow = a.o + qoff + (int64_t)qrow * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -362,7 +457,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
       }
     if (hh == 0) {
       const int64_t ri = (int64_t)bh * Nq + qrow;
-      a.lse[ri] = empty ? -INFINITY : (rs.m2 + __log2f(ltot)) * kLn2;
+      a.lse[ri] = empty ? -INFINITY : (rs.m2 + __log2f(ltot) - (FP8 ? 8.f : 0.f)) * kLn2;
       if (STATS) {
         if (a.dupcnt) a.dupcnt[ri] = empty ? 0 : rs.run_cnt;
         if (a.ones) a.ones[ri] = empty ? 0 : ones_tot;
@@ -394,10 +489,79 @@ static hipError_t launch_fwd_mode(const FwdArgs& a, int mode, bool stats, bool k
   return kahan ? launch_fwd_m<E, D, CAUSAL, false, true>(a, mode, s) : launch_fwd_m<E, D, CAUSAL, false, false>(a, mode, s);
 }
 
+#if FA_ELEM == 2
+// V for the FP8 P^ V forward: one workgroup per (head, 128-key block).  The block's largest
+// magnitude sets its scale s = amax / 448 (s = 1 for an all-zero block), and each value is stored
+// as E4M3(v / s), round to nearest even.  Output per block: D rows (one per head dimension) of
+// 128 bytes; byte 64 ck + 32 h + 4 sl + t of a row holds key 64 ck + 32 (sl / 4) + 8 (sl % 4) +
+// 4 h + t of the block, which is the order in which the forward's P^ registers hold the keys of
+// a 64-key chunk for lane half h (slot sl, byte t).  Keys past Nk are stored as 0.
+template <int D>
+__global__ __launch_bounds__(256) void v8_pack_kernel(const uint16_t* __restrict__ v, uint8_t* __restrict__ v8,
+                                                      float* __restrict__ vscale, int Nk, int n_vblk) {
+  constexpr int BK = 128;
+  __shared__ __attribute__((aligned(16))) uint16_t sv[BK * D];
+  __shared__ float red[4];
+  const int bh = blockIdx.x / n_vblk;
+  const int jb = blockIdx.x - bh * n_vblk;
+  const int tid = threadIdx.x;
+  const int rows = min(BK, Nk - jb * BK);
+  const uint16_t* src = v + ((int64_t)bh * Nk + (int64_t)jb * BK) * D;
+  float amax = 0.f;
+  for (int c = tid; c < BK * D / 8; c += 256) {
+    i32x4 w = {0, 0, 0, 0};
+    if (c / (D / 8) < rows) w = *reinterpret_cast<const i32x4*>(src + (int64_t)c * 8);
+    *reinterpret_cast<i32x4*>(&sv[c * 8]) = w;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const f32x2 f = unpack2<kElemBf16>((uint32_t)w[t]);
+      amax = fmaxf(amax, fmaxf(fabsf(f[0]), fabsf(f[1])));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float sc = amax > 0.f ? amax / 448.f : 1.f;
+  const float inv = 1.f / sc;
+  if (tid == 0) vscale[(int64_t)bh * n_vblk + jb] = sc;
+  uint8_t* dst = v8 + ((int64_t)bh * n_vblk + jb) * (D * BK);
+  for (int ch = tid; ch < D * 8; ch += 256) {
+    const int d = ch >> 3, c = ch & 7;
+    i32x4 out;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      float x[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int pos = 16 * c + 4 * q4 + t;
+        const int ck = pos >> 6, h = (pos >> 5) & 1, sl = (pos >> 2) & 7;
+        const int key = 64 * ck + 32 * (sl >> 2) + 8 * (sl & 3) + 4 * h + t;
+        x[t] = __builtin_bit_cast(float, (uint32_t)sv[key * D + d] << 16) * inv;
+      }
+      out[q4] = (int)pack4_fp8(x[0], x[1], x[2], x[3]);
+    }
+    *reinterpret_cast<i32x4*>(dst + (int64_t)d * BK + 16 * c) = out;
+  }
+}
+
+hipError_t launch_v8_pack(const uint16_t* v, uint8_t* v8, float* vscale, int BH, int Nk, int d, hipStream_t s) {
+  const int n_vblk = (Nk + 127) / 128;
+  if (BH == 0 || n_vblk == 0) return hipSuccess;
+  const dim3 grid((unsigned)((int64_t)BH * n_vblk));
+  if (d == 64)
+    hipLaunchKernelGGL((v8_pack_kernel<64>), grid, dim3(256), 0, s, v, v8, vscale, Nk, n_vblk);
+  else
+    hipLaunchKernelGGL((v8_pack_kernel<128>), grid, dim3(256), 0, s, v, v8, vscale, Nk, n_vblk);
+  return hipGetLastError();
+}
+#endif
+
 #if FA_ELEM == 0
 int fwd_kv_block(int d, bool causal) {
   if (d != 64 && d != 128) return 0;
-  return causal ? fwd_bc<true>() : fwd_bc<false>();
+  return causal ? fwd_bc<kElemBf16, true>() : fwd_bc<kElemBf16, false>();
 }
 int fwd_q_block(int d) { return (d == 64 || d == 128) ? kFwdBr : 0; }
 #endif

@@ -25,6 +25,9 @@ struct FwdArgs {
   float sl2;        // scale * log2(e)
   float scale;
   float beta;
+  const uint8_t* v8;    // FP8 P^ V only: V as E4M3 blocks written by launch_v8_pack
+  const float* vscale;  // FP8 P^ V only: one scale per (head, 128-key block)
+  int n_vblk;           // FP8 P^ V only: 128-key blocks per head
 };
 
 struct BwdArgs {
@@ -58,6 +61,9 @@ hipError_t launch_bwd_dkdv(BwdArgs a, int d, bool causal, hipStream_t s);
 template <int E>
 hipError_t launch_bwd_dq(BwdArgs a, int d, bool causal, hipStream_t s);
 int fwd_kv_block(int d, bool causal);
+// FP8 P^ V: quantise V ([BH, Nk, d] bf16) into v8 ([BH, ceil(Nk / 128), d, 128] bytes) and
+// vscale ([BH, ceil(Nk / 128)] fp32).  Defined in the FA_ELEM = 2 instance of fa_fwd.hip.
+hipError_t launch_v8_pack(const uint16_t* v, uint8_t* v8, float* vscale, int BH, int Nk, int d, hipStream_t s);
 hipError_t launch_mfma_peak(float* out, int n_workgroups, int iters, hipStream_t stream);
 int fwd_q_block(int d);
 

@@ -241,3 +241,20 @@ def test_binding_rejects_mixed_or_unsupported_dtypes():
         fa._elem(torch.zeros(1, dtype=torch.float32), "q")
     assert fa._elem(torch.zeros(1, dtype=torch.float16), "q") == fa.FA_ELEM_F16
     assert fa._elem(torch.zeros(1, dtype=torch.bfloat16), "q") == fa.FA_ELEM_BF16
+
+
+def test_fp8pv_entry_point_validates(lib, ffi):
+    def call(ws=P, q=P, B=1, H=2, Nq=128, Nk=300, d=64, causal=1, flag=1, flags=0):
+        return lib.fa_fwd_fp8pv(q, P, P, P, P, None, None, None, None, ws, B, H, Nq, Nk, d, causal,
+                                0.125, 1.25, flag, flags, None)
+    assert call(ws=None) == ffi.FA_ERR_NULL
+    assert call(ws=MIS) == ffi.FA_ERR_ALIGN
+    assert call(q=None) == ffi.FA_ERR_NULL
+    assert call(d=96) == ffi.FA_ERR_HEADDIM and call(flag=3) == ffi.FA_ERR_PARAM
+    assert call(causal=3) == ffi.FA_ERR_PARAM and call(flags=2) == ffi.FA_ERR_PARAM
+    assert call(ws=None, Nk=0) != ffi.FA_ERR_NULL  # no keys: no workspace needed
+    assert call(B=0, q=None, ws=None) == ffi.FA_OK
+    assert lib.fa_fwd_fp8pv_workspace_bytes(1, 2, 300, 64) == 2 * 3 * (64 * 128 + 4)
+    assert lib.fa_fwd_fp8pv_workspace_bytes(1, 32, 8192, 128) == 32 * 64 * (128 * 128 + 4)
+    assert lib.fa_fwd_fp8pv_workspace_bytes(1, 1, 0, 128) == 0
+    assert lib.fa_fwd_fp8pv_workspace_bytes(1, 1, 8, 80) == 0
