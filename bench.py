@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--config", type=int, default=4, help="workload id (1-5)")
     ap.add_argument("--mode", type=int, default=1, help="stable_flag: 0, 1 or 2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8pv", action="store_true",
+                    help="skip the FP8 P^V forward leg (fa_fwd_fp8pv on the same bf16 inputs)")
     ap.add_argument("--no-f16", action="store_true",
                     help="skip the fp16 leg (the same workload with fp16 inputs, reported beside "
                          "the bf16 headline)")
@@ -212,6 +214,28 @@ def main():
     ff = fwd_flops(B, H, N, d, causal)
     total = 3.5 * ff
 
+    # FP8 P^V leg: the forward with its P^ V product in E4M3 (V quantised per 128-key block by the
+    # library's pre-pass, which runs inside the timed call), on the same bf16 inputs.
+    fp8pv = None
+    if not args.no_fp8pv:
+        ws8 = torch.empty(fa.fa_fwd_fp8pv_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+        o8 = torch.empty_like(q)
+
+        def fwd8():
+            fa.fa_fwd_fp8pv(q, k, v, o8, lse, None, None, None, None, ws8, int(causal), scale, 1.25,
+                            mode, stream=stream)
+
+        for _ in range(args.warmup):
+            fwd8()
+        ms8 = time_events(fwd8, it, stream)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o8.float()).all()
+        fp8pv = {"fwd_ms": ms8, "fwd_TFLOP/s": ff / (ms8 * 1e-3) / 1e12,
+                 "fwd_frac_bf16_peak": ff / (ms8 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                 "max_abs_diff_to_bf16_O": float((o8.float() - o.float()).abs().max())}
+        del ws8, o8
+        run_fwd()  # restore this mode's lse
+
     # fp16 leg: the same draws rounded to fp16 (fa_fwd_elem / fa_bwd_elem), whole step and
     # forward alone, after the bf16 measurements.
     f16 = None
@@ -309,6 +333,8 @@ def main():
     }
     if f16 is not None:
         out["f16"] = f16
+    if fp8pv is not None:
+        out["fp8pv"] = fp8pv
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, t, mode)
     print(json.dumps(out), flush=True)

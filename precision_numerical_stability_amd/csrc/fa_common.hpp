@@ -239,8 +239,11 @@ struct DirectStage {
     }
   }
   // As issue, with this lane's offsets formed on the spot instead of read from voff (for kernels
-  // short of registers); needs only `wave` set.
+  // short of registers); needs only `wave` set.  The lane index passes through an empty asm
+  // statement so the compiler cannot hoist the offsets out of the caller's loop (it would keep
+  // them live across the loop, which is what this variant avoids).
   __device__ __forceinline__ void issue_lazy(const uint16_t* head, int row0, int n_rows, uint32_t lds, int lane) {
+    asm volatile("" : "+v"(lane));
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int p = (wave * kPer + i) * 64 + lane;

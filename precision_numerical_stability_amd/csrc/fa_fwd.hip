@@ -116,7 +116,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   i32x8 pk8[FP8 ? KB / 2 : 1];
 
   DirectStage<BC, D, kFwdThreads / 2> stg;  // group A's threads stage every tile
-  stg.init(tid & (kFwdThreads / 2 - 1));
+  // The FP8 instances are shorter of registers: they form the staging offsets at issue.
+  if constexpr (FP8) stg.wave = __builtin_amdgcn_readfirstlane((tid & (kFwdThreads / 2 - 1)) >> 6);
+  else stg.init(tid & (kFwdThreads / 2 - 1));
   // FP8 P^ V: the V block is D rows (one per head dimension) of 128 E4M3 bytes, staged like a
   // D x 64 tile of 16-bit elements.
   DirectStage<D, 64, kFwdThreads / 2> stg8;  // offsets formed at issue (no registers held)
@@ -125,7 +127,10 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   const float* VSg = FP8 ? a.vscale + (int64_t)bh * a.n_vblk : nullptr;
   constexpr uint32_t kTileBytes = BC * D * 2;
   const uint32_t aK = lds_addr(&sK[0][0]), aV = lds_addr(&sV[0][0]);
-  if (grp == 0) stg.issue(Kg, 0, Nk, aK);
+  if (grp == 0) {
+    if constexpr (FP8) stg.issue_lazy(Kg, 0, Nk, aK, lane);
+    else stg.issue(Kg, 0, Nk, aK);
+  }
   // Everyone waits here: the Q fragments above are then known complete, so no wait for them is
   // left inside the loop (where the tile loads would make it wait for those as well).
   wait_vm0();
@@ -141,12 +146,12 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   // first only reads, the second reads and multiplies).
   constexpr int KK = FP8 ? 2 * (BC / 64) : BC / 16;
   constexpr int NPV = DT * KK, NSS = KB * KS;
-  constexpr int MDEPTH = FP8 ? 3 : 4, MRING = MDEPTH + 1;
+  constexpr int MDEPTH = FP8 ? 2 : 4, MRING = MDEPTH + 1;
   e16x8 mring[MRING];
-  // FP8 instances: step k's operand is half k & 1 of mring8[(k / 2) % 3], so the two 16-byte
+  // FP8 instances: step k's operand is half k & 1 of mring8[(k / 2) % 2], so the two 16-byte
   // reads of one k = 64 MFMA fill one 8-register tuple.  At step k the MFMA still uses step k - 1's
-  // half while the read for step k + MDEPTH is issued: MDEPTH + 2 steps in flight, 6 positions.
-  constexpr int R8 = 3;
+  // half while the read for step k + MDEPTH is issued: MDEPTH + 2 steps in flight, 4 positions.
+  constexpr int R8 = 2;
   static_assert(!FP8 || 2 * R8 >= MDEPTH + 2, "ring positions must cover the steps in flight");
   i32x8 mring8[R8];
   auto ring_put = [&](auto kc, e16x8 x) __attribute__((always_inline)) {
@@ -407,7 +412,10 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   // for both at the end of its V(j), before K_{j+1} and V_j are read in phase 2j+2.
   auto iteration = [&](int j, auto par_tag) __attribute__((always_inline)) {
     constexpr int PAR = decltype(par_tag)::value;
-    if (grp == 0 && j + 1 < n_kv) stg.issue(Kg, (j + 1) * BC, Nk, aK + (PAR ^ 1) * kTileBytes);
+    if (grp == 0 && j + 1 < n_kv) {
+      if constexpr (FP8) stg.issue_lazy(Kg, (j + 1) * BC, Nk, aK + (PAR ^ 1) * kTileBytes, lane);
+      else stg.issue(Kg, (j + 1) * BC, Nk, aK + (PAR ^ 1) * kTileBytes);
+    }
     matrix_phase(j, par_tag);
     __syncthreads();
     if constexpr (FP8) {
