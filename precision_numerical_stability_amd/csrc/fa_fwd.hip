@@ -179,8 +179,13 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
       return mring[k % MRING];
     }
   };
+  // Lane coordinates the operand reads use.  The FP8 instances re-derive them at the start of each
+  // matrix phase from a value the compiler cannot see through, so the per-lane LDS addresses are
+  // formed there and die with the phase instead of staying live (and spilling) across the loop.
+  int mlane = lane, ml32 = l32, mhh = hh;
   auto m_read = [&](auto kc, const uint16_t* tV, const uint16_t* tK) __attribute__((always_inline)) {
     constexpr int k = decltype(kc)::value;
+    const int lane = mlane, l32 = ml32, hh = mhh;
     if constexpr (k < NPV && FP8) {
       // Row 32 dt + l32 of the V block, bytes 64 ck + 32 hh + 16 part: the 32 keys of this lane
       // half, in the order P^ sits in its accumulator registers (v8_pack_kernel writes them so).
@@ -251,6 +256,12 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
     const uint16_t* tK = sK[PAR];
     const bool pv = j >= 1 && j - 1 < n_mine;
     const bool sc = j < n_mine;
+    if constexpr (FP8) {
+      mlane = lane;
+      asm volatile("" : "+v"(mlane));
+      ml32 = mlane & 31;
+      mhh = mlane >> 5;
+    }
     __builtin_amdgcn_s_setprio(1);
     if (pv) m_stream(c0{}, cpv{}, tV, tK);
     if (sc) m_stream(cpv{}, cend{}, tV, tK);
@@ -351,7 +362,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
     float oscale = alpha;
     if constexpr (FP8) {
       const float vs = VSg[j];
-      oscale = alpha * (rs.vs / vs);
+      oscale = alpha * (rs.vs * __builtin_amdgcn_rcpf(vs));  // O's rescale need not be exact
       rs.vs = vs;
     }
     // FP8: P^ is formed as 2^8 P^ (exponent offset folded into the FMA) for its E4M3 rounding;
@@ -416,11 +427,14 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
       if constexpr (FP8) stg.issue_lazy(Kg, (j + 1) * BC, Nk, aK + (PAR ^ 1) * kTileBytes, lane);
       else stg.issue(Kg, (j + 1) * BC, Nk, aK + (PAR ^ 1) * kTileBytes);
     }
-    matrix_phase(j, par_tag);
-    __syncthreads();
+    // FP8: the V block is issued here too, so that forming its staging offsets stays out of the
+    // vector phase (its buffer held V_{j-2}, last read in phase 2j - 1, as for the K buffer).
     if constexpr (FP8) {
       if (grp == 0 && j < n_kv) stg8.issue_lazy(V8g, j * D, a.n_vblk * D, aV + PAR * kTileBytes, lane);
-    } else {
+    }
+    matrix_phase(j, par_tag);
+    __syncthreads();
+    if constexpr (!FP8) {
       if (grp == 0 && j < n_kv) stg.issue(Vg, j * BC, Nk, aV + PAR * kTileBytes);
     }
     vector_phase(j);
