@@ -522,7 +522,10 @@ template <int D>
 __global__ __launch_bounds__(256) void v8_pack_kernel(const uint16_t* __restrict__ v, uint8_t* __restrict__ v8,
                                                       float* __restrict__ vscale, int Nk, int n_vblk) {
   constexpr int BK = 128;
-  __shared__ __attribute__((aligned(16))) uint16_t sv[BK * D];
+  // Rows padded by 8 elements (16 bytes): the gather below reads 16 keys at one column, which a
+  // 2D-byte stride would put in a single bank.
+  constexpr int LD = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t sv[BK * LD];
   __shared__ float red[4];
   const int bh = blockIdx.x / n_vblk;
   const int jb = blockIdx.x - bh * n_vblk;
@@ -533,7 +536,7 @@ __global__ __launch_bounds__(256) void v8_pack_kernel(const uint16_t* __restrict
   for (int c = tid; c < BK * D / 8; c += 256) {
     i32x4 w = {0, 0, 0, 0};
     if (c / (D / 8) < rows) w = *reinterpret_cast<const i32x4*>(src + (int64_t)c * 8);
-    *reinterpret_cast<i32x4*>(&sv[c * 8]) = w;
+    *reinterpret_cast<i32x4*>(&sv[(c / (D / 8)) * LD + (c % (D / 8)) * 8]) = w;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const f32x2 f = unpack2<kElemBf16>((uint32_t)w[t]);
@@ -560,7 +563,7 @@ __global__ __launch_bounds__(256) void v8_pack_kernel(const uint16_t* __restrict
         const int pos = 16 * c + 4 * q4 + t;
         const int ck = pos >> 6, h = (pos >> 5) & 1, sl = (pos >> 2) & 7;
         const int key = 64 * ck + 32 * (sl >> 2) + 8 * (sl & 3) + 4 * h + t;
-        x[t] = __builtin_bit_cast(float, (uint32_t)sv[key * D + d] << 16) * inv;
+        x[t] = __builtin_bit_cast(float, (uint32_t)sv[key * LD + d] << 16) * inv;
       }
       out[q4] = (int)pack4_fp8(x[0], x[1], x[2], x[3]);
     }
