@@ -506,3 +506,61 @@ def test_no_keys_and_no_queries(fa):
     fa.fa_bwd_qk(q0, k, k, o, lse, q0, q0.clone(), dk, dv, torch.empty((1, 2, 0), device=DEV), 2, 0.125)
     torch.cuda.synchronize()
     assert torch.all(dk == 0) and torch.all(dv == 0)
+
+
+def test_graph_capture_replays_match_eager(fa):
+    """fa_fwd_qk + fa_bwd_qk (and the FP8 P^V forward) captured into one HIP graph: the library
+    only launches kernels (no memset, no allocation), so every replay, with eager work and
+    synchronisations in between and fresh inputs copied in before some of them, equals the eager
+    result bit for bit."""
+    _say("graph-capture")
+    B, H, N, d = 1, 4, 640, 128
+    scale = d ** -0.5
+    srcs = [{k_: v_.to(DEV) for k_, v_ in rect_inputs(B, H, N, N, d, seed=2100 + i).items()} for i in range(2)]
+    st = {k_: v_.clone() for k_, v_ in srcs[0].items()}  # static input buffers the graph reads
+    o, lse = torch.empty_like(st["q"]), torch.empty((B, H, N), device=DEV)
+    dq, dk, dv = (torch.empty_like(st["q"]) for _ in range(3))
+    delta = torch.empty_like(lse)
+    o8, lse8 = torch.empty_like(st["q"]), torch.empty_like(lse)
+    ws8 = torch.empty(fa.fa_fwd_fp8pv_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=DEV)
+
+    def run(stream=None):
+        fa.fa_fwd_qk(st["q"], st["k"], st["v"], o, lse, None, None, None, None, 1, scale, BETA, 1,
+                     stream=stream)
+        fa.fa_bwd_qk(st["q"], st["k"], st["v"], o, lse, st["do"], dq, dk, dv, delta, 1, scale,
+                     stream=stream)
+        fa.fa_fwd_fp8pv(st["q"], st["k"], st["v"], o8, lse8, None, None, None, None, ws8, 1, scale,
+                        BETA, 1, stream=stream)
+
+    def snapshot():
+        return [t.clone() for t in (o, lse, dq, dk, dv, o8, lse8)]
+
+    eager = []
+    for src in srcs:
+        for k_ in st:
+            st[k_].copy_(src[k_])
+        run()
+        torch.cuda.synchronize()
+        eager.append(snapshot())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run(stream=s)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        run(stream=s)
+    for rep in range(6):
+        which = rep % 2
+        for k_ in st:
+            st[k_].copy_(srcs[which][k_])
+        junk = torch.randn(1 << 20, device=DEV).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        for t in (o, lse, dq, dk, dv, o8, lse8):
+            t.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(snapshot(), eager[which]):
+            assert torch.equal(got, want), f"replay {rep} differs from the eager result"
+        assert torch.isfinite(junk)
