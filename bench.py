@@ -131,9 +131,9 @@ def cpu_baseline(cfg, t, mode, budget_s=15.0):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the attention heads of this "
-              "workload shard across GPUs without communication, and this build measures the "
-              "one-GPU kernel.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the attention heads of "
+              "this workload shard across GPUs without communication, so the figure that matters "
+              "is the one-GPU kernel on its share of the heads (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
     import torch
     import precision_numerical_stability_amd as fa

@@ -1,0 +1,35 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU contract, the flop convention and the lookup
+of recorded HBM traffic by source digest."""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr and res.stdout == ""
+
+
+def test_flop_convention():
+    # FA convention: 4 B H N^2 d, halved when causal; the benchmark shape gives 549.76 GFLOP forward
+    assert bench.fwd_flops(1, 32, 8192, 128, True) == 4 * 32 * 8192 ** 2 * 128 / 2 == 549755813888
+    assert bench.fwd_flops(1, 1, 128, 64, False) == 4 * 128 * 128 * 64
+
+
+def test_recorded_traffic_follows_the_source_digest(tmp_path, monkeypatch):
+    digest = bench.sources_digest("dkdv")
+    f = tmp_path / "traffic.md"
+    f.write_text("| kernel | sources digest | fetched MB | written MB | traffic MB | alg | ratio |\n"
+                 "|---|---|---|---|---|---|---|\n"
+                 f"| dkdv | {digest} | 700.0 | 100.0 | 800.0 | 1 + 1 | 2.0 |\n"
+                 "| dq | 0123456789abcdef | 1.0 | 1.0 | 2.0 | 1 + 1 | 1.0 |\n")
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.recorded_traffic("dkdv") == 800.0e6
+    assert bench.recorded_traffic("dq") is None  # recorded for other sources: not reported
+    assert bench.recorded_traffic("fwd") is None
