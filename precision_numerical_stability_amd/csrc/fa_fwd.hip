@@ -6,7 +6,9 @@
 // 训练稳定性优化实践" (jsqmd.com/news/761560) §3.2: Q K^T accumulated in fp32, softmax in fp32,
 // P^ rounded to the 16-bit element type for the product with V.  That article names both 16-bit
 // formats; the element type (bf16 or fp16) is a template parameter, and this file is compiled once
-// per element type (FA_ELEM).
+// per element type (FA_ELEM).  A third instance (FA_ELEM = 2) is the bf16 forward with the P^ V
+// product in FP8 E4M3, the lower precision the article's §6.1 extends the method to, together with
+// the kernel that quantises V for it (v8_pack_kernel).
 //
 // Work split: one workgroup of 8 waves per (query tile of 256 rows, head).  Each wave owns 32
 // queries and computes S^T = K Q^T, so each lane owns one query column: its row max, repeat count
