@@ -499,41 +499,56 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   // The masked blocks (the causal leading ones, one or two of them, and a ragged last block) run
   // through the masked body outside the main loop, so the loop body has a single variant and
   // the accumulators need no copies at branch joins.
+  //
+  // Query block i lives in LDS buffer (i - i_first + b0) & 1.  b0 is chosen so that the unmasked
+  // loop starts in buffer 0: that loop is unrolled by two, so each of its steps knows its buffer
+  // at compile time and the LDS addresses fold into instruction offsets (with a run-time buffer
+  // every operand read needs its address rebuilt).  The masked steps, at most three per
+  // workgroup, index the buffers at run time.
+  const int n_full = Nq / BQ;  // blocks lying entirely inside the sequence
+  // Leading masked blocks: at most two, since their 127 query rows span at most two 128-row blocks.
+  const int n_lead = CAUSAL ? min(2, max(0, i_lead - i_first)) : 0;
   int i = i_first;
-  int buf = 0;
-  auto step = [&](auto mask_tag) __attribute__((always_inline)) {
+  int buf = n_lead & 1;
+  auto step = [&](auto mask_tag, auto buf_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    const int b = buf_tag;  // a constant in the unmasked loop, a run-time value in masked steps
     const int q0 = i * BQ;
     const bool has_next = (i + 1 < n_q);
     if (has_next) {
-      st.issue(Qg, q0 + BQ, Nq, aQ + (buf ^ 1) * kTileBytes);
-      st.issue(Gg, q0 + BQ, Nq, aG + (buf ^ 1) * kTileBytes);
+      st.issue(Qg, q0 + BQ, Nq, aQ + (b ^ 1) * kTileBytes);
+      st.issue(Gg, q0 + BQ, Nq, aG + (b ^ 1) * kTileBytes);
       load_rows(i + 1);
     }
-    dkdv_block<E, D, CAUSAL, MASK>(sQ[buf], sG[buf], sL[buf], sD[buf], q0, Nq, a.coff, key, lane, a.sl2, f, dk, dv);
-    if (has_next) store_rows(buf ^ 1);
+    dkdv_block<E, D, CAUSAL, MASK>(sQ[b], sG[b], sL[b], sD[b], q0, Nq, a.coff, key, lane, a.sl2, f, dk, dv);
+    if (has_next) store_rows(b ^ 1);
     wait_vm0();
     __syncthreads();
     ++i;
-    buf ^= 1;
+    buf = b ^ 1;
   };
   using masked = std::integral_constant<bool, true>;
   using plain = std::integral_constant<bool, false>;
+  using buf0 = std::integral_constant<int, 0>;
+  using buf1 = std::integral_constant<int, 1>;
 
   if (i < n_q) {
-    st.issue(Qg, i * BQ, Nq, aQ);
-    st.issue(Gg, i * BQ, Nq, aG);
+    st.issue(Qg, i * BQ, Nq, aQ + buf * kTileBytes);
+    st.issue(Gg, i * BQ, Nq, aG + buf * kTileBytes);
     load_rows(i);
-    store_rows(0);
+    store_rows(buf);
   }
   wait_vm0();
   __syncthreads();
-  const int n_full = Nq / BQ;  // blocks lying entirely inside the sequence
-  // At most two leading masked blocks: their 127 query rows span at most two 128-row blocks.
-  if (CAUSAL && i < i_lead) step(masked{});
-  if (CAUSAL && i < i_lead) step(masked{});
-  while (i < n_full) step(plain{});
-  if (i < n_q) step(masked{});
+  if (CAUSAL && i < i_lead) step(masked{}, buf);
+  if (CAUSAL && i < i_lead) step(masked{}, buf);
+  // buf == 0 here (n_lead steps from b0 = n_lead & 1).
+  while (i + 1 < n_full) {
+    step(plain{}, buf0{});
+    step(plain{}, buf1{});
+  }
+  if (i < n_full) step(plain{}, buf0{});
+  if (i < n_q) step(masked{}, buf);
 
   if (key < Nk) {
     uint16_t* dkr = a.dk + koff + (int64_t)key * D;
