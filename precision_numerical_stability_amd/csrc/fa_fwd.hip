@@ -27,6 +27,7 @@
 // when causal, 64 otherwise) are double-buffered in LDS: K_{j+1} and V_j are loaded during phase
 // 2j; K_j is read in phases 2j (A) and 2j+1 (B), V_j in phases 2j+2 (A) and 2j+3 (B).  Longer
 // blocks halve the barriers per key; the non-causal instances run out of registers at 128.
+#include <climits>
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -274,17 +275,18 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   auto vector_phase = [&](int j) __attribute__((always_inline)) {
     if (j >= n_mine) return;
     if (j >= n_plain) {
-      // Key indices are taken relative to coff (all scalar arithmetic), so the causal test
-      // compares with the lane's query directly: key - coff > qrow.
+      // Element (kb, r) holds key kv0 + c + 4 hh, c = 32 kb + 8 (r / 4) + r % 4, with key indices
+      // taken relative to coff (kv0 = block start - coff).  It is hidden past the last key or
+      // (causal) past the lane's query, i.e. when c > lim: one compare per element against a
+      // per-lane bound formed here, so nothing extra stays live across the loop.
       const int kv0 = j * BC - a.coff;
-      const int nk = Nk - a.coff;
+      const int lim = min(CAUSAL ? qrow - kv0 : INT_MAX, Nk - a.coff - 1 - kv0) - 4 * hh;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const bool hide = (key >= nk) || (CAUSAL && key > qrow);
-          s[kb][r] = hide ? -INFINITY : s[kb][r];
+          const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
+          s[kb][r] = (c > lim) ? -INFINITY : s[kb][r];
         }
     }
     if (STATS) {
