@@ -204,6 +204,14 @@ def main():
     fa.fa_probe_mfma_peak(probe_out, n_wg, iters, stream=stream)
     ms_probe = time_events(lambda: fa.fa_probe_mfma_peak(probe_out, n_wg, iters, stream=stream), 3, stream)
     mfma_peak_meas = n_wg * 4 * iters * 32 * 32768 / (ms_probe * 1e-3) / 1e12
+    # LDS read ceiling: two 64 KiB workgroups per CU, each wave reading 16 KiB per iteration.
+    n_lds, it_lds = 2 * 256, 4096
+    fa.fa_probe_lds_read(probe_out, n_lds, it_lds, stream=stream)
+    ms_lds = time_events(lambda: fa.fa_probe_lds_read(probe_out, n_lds, it_lds, stream=stream), 3, stream)
+    lds_tbs = n_lds * 4 * it_lds * 16384 / (ms_lds * 1e-3) / 1e12
+    # Per CU and clock, at the clock the MFMA probe implies (published peak at 2.4 GHz).
+    clk_ghz = 2.4 * mfma_peak_meas / PEAK_BF16_TFLOPS
+    lds_b_per_clk = lds_tbs * 1e12 / 256 / (clk_ghz * 1e9)
     csrc_t = torch.empty(256 << 20, dtype=torch.float32, device=dev)
     cdst_t = torch.empty_like(csrc_t)
     cdst_t.copy_(csrc_t)
@@ -339,7 +347,8 @@ def main():
             str(mode): {"ms": ms_step, "TFLOP/s": value, "frac_bf16_peak": value / PEAK_BF16_TFLOPS},
             str(other): {"ms": ms_step_other, "TFLOP/s": total / (ms_step_other * 1e-3) / 1e12,
                          "frac_bf16_peak": total / (ms_step_other * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}},
-        "measured_ceilings": {"mfma_bf16_TFLOP/s": mfma_peak_meas, "d2d_copy_GB/s": copy_gbs},
+        "measured_ceilings": {"mfma_bf16_TFLOP/s": mfma_peak_meas, "d2d_copy_GB/s": copy_gbs,
+                              "lds_read_TB/s": lds_tbs, "lds_read_B_per_clk_per_CU": lds_b_per_clk},
         "fwdbwd_frac_measured_mfma": value / mfma_peak_meas,
         "exact_causal_pairs": pairs,
         "kernels": kernels,

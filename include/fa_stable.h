@@ -231,6 +231,14 @@ int fa_fwd_kv_block(int d, int causal);
  * FA_ERR_PARAM (n_workgroups outside 1 .. 2^20 or iters < 1), FA_ERR_ALIGN, FA_ERR_HIP. */
 int fa_probe_mfma_peak(float* out, int n_workgroups, int iters, void* stream);
 
+/* Measurement helper, not part of the attention path: runs n_workgroups workgroups of 256
+ * threads holding 64 KiB of LDS each (two per CU), each wave reading iters * 16 KiB of LDS with
+ * conflict-free 16-byte reads, and writes one float per thread to out (caller-owned device
+ * memory of n_workgroups * 256 floats, 4-byte aligned; the values are meaningless).  Timing it
+ * gives the LDS read bandwidth the GPU sustains, the ceiling of the kernels' LDS operand reads.
+ * Errors: as fa_probe_mfma_peak. */
+int fa_probe_lds_read(float* out, int n_workgroups, int iters, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* fa_status_str(int status);
 

@@ -39,7 +39,7 @@ __all__ = [
     "fa_fwd", "fa_fwd_ex", "fa_fwd_stats", "fa_fwd_qk", "fa_fwd_elem", "FA_FWD_COMPENSATED_SUM",
     "fa_bwd", "fa_bwd_ex", "fa_bwd_qk", "fa_bwd_elem", "FA_ELEM_BF16", "FA_ELEM_F16",
     "fa_fwd_fp8pv", "fa_fwd_fp8pv_workspace_bytes", "forward_fp8pv",
-    "fa_bwd_workspace_bytes", "fa_fwd_kv_block", "fa_probe_mfma_peak",
+    "fa_bwd_workspace_bytes", "fa_fwd_kv_block", "fa_probe_mfma_peak", "fa_probe_lds_read",
     "FA_CAUSAL_NONE", "FA_CAUSAL_TOP_LEFT", "FA_CAUSAL_BOTTOM_RIGHT", "fa_status_str",
     "fa_last_hip_error", "FaError", "forward", "backward", "attention", "STANDARD", "TIE_RULE",
     "TIE_ANTICIPATE", "DEFAULT_BETA", "library_path",
@@ -83,6 +83,18 @@ def fa_probe_mfma_peak(out, n_workgroups: int, iters: int, stream=None) -> None:
         raise ValueError("out must be a float32 CUDA tensor of n_workgroups * 256 elements")
     st = _stream_handle(out.device, stream)
     rc = _lib.fa_probe_mfma_peak(_ptr(out), int(n_workgroups), int(iters), st)
+    if rc != FA_OK:
+        raise FaError(rc)
+
+
+def fa_probe_lds_read(out, n_workgroups: int, iters: int, stream=None) -> None:
+    """Measurement helper (not part of the attention path): n_workgroups x 256 threads, each wave
+    reading iters * 16 KiB of LDS in conflict-free 16-byte reads; out is a float32 CUDA tensor of
+    at least n_workgroups * 256 elements."""
+    if out.dtype != torch.float32 or not out.is_cuda or out.numel() < n_workgroups * 256:
+        raise ValueError("out must be a float32 CUDA tensor of n_workgroups * 256 elements")
+    st = _stream_handle(out.device, stream)
+    rc = _lib.fa_probe_lds_read(_ptr(out), int(n_workgroups), int(iters), st)
     if rc != FA_OK:
         raise FaError(rc)
 

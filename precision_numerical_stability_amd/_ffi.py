@@ -50,6 +50,7 @@ SIGNATURES = {
     "fa_fwd_fp8pv_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "fa_fwd_kv_block": (_I, [_I, _I]),
     "fa_probe_mfma_peak": (_I, [_P, _I, _I, _P]),
+    "fa_probe_lds_read": (_I, [_P, _I, _I, _P]),
     "fa_status_str": (ctypes.c_char_p, [_I]),
     "fa_last_hip_error": (_I, []),
 }

@@ -249,6 +249,13 @@ int fa_probe_mfma_peak(float* out, int n_workgroups, int iters, void* stream) {
   return hip_status(fa::launch_mfma_peak(out, n_workgroups, iters, static_cast<hipStream_t>(stream)));
 }
 
+int fa_probe_lds_read(float* out, int n_workgroups, int iters, void* stream) {
+  if (!out) return FA_ERR_NULL;
+  if (n_workgroups < 1 || iters < 1 || n_workgroups > (1 << 20)) return FA_ERR_PARAM;
+  if (!aligned(out, 4)) return FA_ERR_ALIGN;
+  return hip_status(fa::launch_lds_read(out, n_workgroups, iters, static_cast<hipStream_t>(stream)));
+}
+
 const char* fa_status_str(int status) {
   switch (status) {
     case FA_OK: return "FA_OK";

@@ -65,6 +65,7 @@ int fwd_kv_block(int d, bool causal);
 // vscale ([BH, ceil(Nk / 128)] fp32).  Defined in the FA_ELEM = 2 instance of fa_fwd.hip.
 hipError_t launch_v8_pack(const uint16_t* v, uint8_t* v8, float* vscale, int BH, int Nk, int d, hipStream_t s);
 hipError_t launch_mfma_peak(float* out, int n_workgroups, int iters, hipStream_t stream);
+hipError_t launch_lds_read(float* out, int n_workgroups, int iters, hipStream_t stream);
 int fwd_q_block(int d);
 
 }  // namespace fa

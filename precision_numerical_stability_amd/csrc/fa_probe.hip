@@ -1,7 +1,9 @@
-// Measurement helper: the dense bf16 MFMA rate the GPU sustains under full load, against which
-// the attention kernels' rates are reported beside the published peak.  Each wave runs four
-// independent accumulator chains of v_mfma_f32_32x32x16_bf16 on register operands (no memory
-// traffic inside the loop) and writes one value per lane so the work cannot be dropped.
+// Measurement helpers: the dense bf16 MFMA rate and the LDS read bandwidth the GPU sustains under
+// full load, against which the attention kernels' rates are reported beside the published peaks.
+// The MFMA probe runs four independent accumulator chains of v_mfma_f32_32x32x16_bf16 per wave on
+// register operands (no memory traffic inside the loop); the LDS probe issues 16-byte reads
+// (the width of the kernels' operand reads) at consecutive addresses, so no bank conflicts.
+// Each writes one value per lane so the work cannot be dropped.
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -34,6 +36,35 @@ __global__ __launch_bounds__(kProbeThreads) void mfma_peak_kernel(float* out, in
 
 hipError_t launch_mfma_peak(float* out, int n_workgroups, int iters, hipStream_t stream) {
   hipLaunchKernelGGL(mfma_peak_kernel, dim3(n_workgroups), dim3(kProbeThreads), 0, stream, out, iters);
+  return hipGetLastError();
+}
+
+// 64 KiB of LDS per workgroup, so two workgroups (eight waves) share a CU.  Each wave reads
+// 16 KiB per iteration: sixteen 16-byte reads per lane, at an offset that changes with the
+// iteration so the reads cannot be moved out of the loop.  Every address stays below 40 KiB.
+constexpr int kLdsProbeInts = 16384;
+
+__global__ __launch_bounds__(kProbeThreads) void lds_read_kernel(float* out, int iters) {
+  __shared__ __attribute__((aligned(16))) int buf[kLdsProbeInts];
+  for (int i = threadIdx.x; i < kLdsProbeInts; i += kProbeThreads) buf[i] = (int)(i * 2654435761u);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  int acc = 0;
+  for (int it = 0; it < iters; ++it) {
+    int base = (it & 3) * 8192 + lane * 16;
+    asm volatile("" : "+v"(base));
+    const char* p = reinterpret_cast<const char*>(buf) + base;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const i32x4 v = *reinterpret_cast<const i32x4*>(p + k * 1024);
+      acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+  }
+  out[(int64_t)blockIdx.x * kProbeThreads + threadIdx.x] = __builtin_bit_cast(float, acc);
+}
+
+hipError_t launch_lds_read(float* out, int n_workgroups, int iters, hipStream_t stream) {
+  hipLaunchKernelGGL(lds_read_kernel, dim3(n_workgroups), dim3(kProbeThreads), 0, stream, out, iters);
   return hipGetLastError();
 }
 

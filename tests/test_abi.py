@@ -146,6 +146,11 @@ def test_probe_rejects_bad_arguments(lib):
     assert lib.fa_probe_mfma_peak(P, 4, 0, None) == 4
     assert lib.fa_probe_mfma_peak(P, (1 << 20) + 1, 4, None) == 4
     assert lib.fa_probe_mfma_peak(ctypes.c_void_p(0x7F0000000002), 4, 4, None) == 5  # FA_ERR_ALIGN
+    assert lib.fa_probe_lds_read(None, 4, 4, None) == 1
+    assert lib.fa_probe_lds_read(P, 0, 4, None) == 4
+    assert lib.fa_probe_lds_read(P, 4, 0, None) == 4
+    assert lib.fa_probe_lds_read(P, (1 << 20) + 1, 4, None) == 4
+    assert lib.fa_probe_lds_read(ctypes.c_void_p(0x7F0000000002), 4, 4, None) == 5
 
 
 def test_fwd_stats_rejects_bad_arguments(lib):
