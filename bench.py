@@ -34,8 +34,8 @@ def fwd_flops(B, H, N, d, causal):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=4, help="workload id (1-5)")
     ap.add_argument("--mode", type=int, default=1, help="stable_flag: 0, 1 or 2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
