@@ -134,10 +134,13 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            int B, int H, int N, int d, int causal, float scale, float beta, int stable_flag,
            void* stream);
 
-/* Backward pass restricted to a subset of its three kernels, in this order when several are set:
+/* Backward pass restricted to a subset of its stages, in this order when several are set:
  *   FA_BWD_DELTA (1): delta_ws = rowsum(dO o O);
  *   FA_BWD_DKDV  (2): dk, dv (reads delta_ws);
  *   FA_BWD_DQ    (4): dq (reads delta_ws).
+ * When FA_BWD_DELTA and FA_BWD_DQ are both set, the dQ kernel forms delta itself (same definition,
+ * fp32, summed in another order, so values may differ from the delta kernel's in the last bits),
+ * stores it in delta_ws and runs before dK/dV; the separate delta kernel is not launched.
  * fa_bwd == fa_bwd_ex(..., FA_BWD_ALL, stream).  Without FA_BWD_DELTA the caller guarantees that
  * delta_ws already holds delta for these o and dO (e.g. from an earlier call).  Pointers of
  * outputs whose stage is not selected are still validated.  stages outside 1..7 -> FA_ERR_PARAM. */

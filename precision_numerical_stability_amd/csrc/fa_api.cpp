@@ -198,7 +198,19 @@ int fa_bwd_elem(const void* q, const void* k, const void* v, const void* o, cons
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool f16 = elem == FA_ELEM_F16;
   int rc = FA_OK;
-  if (stages & FA_BWD_DELTA) {
+  auto run_dq = [&]() {
+    return hip_status(f16 ? fa::launch_bwd_dq<fa::kElemF16>(a, d, causal != 0, s)
+                          : fa::launch_bwd_dq<fa::kElemBf16>(a, d, causal != 0, s));
+  };
+  // With both delta and dQ requested, the dQ kernel forms delta for its rows (it holds dO already)
+  // and runs first, so the delta kernel and one kernel boundary drop out; dK/dV follows.
+  const bool fuse = (stages & FA_BWD_DELTA) && (stages & FA_BWD_DQ);
+  if (fuse) {
+    a.fuse_delta = 1;
+    rc = run_dq();
+    a.fuse_delta = 0;
+    if (rc != FA_OK) return rc;
+  } else if (stages & FA_BWD_DELTA) {
     rc = hip_status(f16 ? fa::launch_bwd_delta<fa::kElemF16>(a, d, s) : fa::launch_bwd_delta<fa::kElemBf16>(a, d, s));
     if (rc != FA_OK) return rc;
   }
@@ -207,9 +219,7 @@ int fa_bwd_elem(const void* q, const void* k, const void* v, const void* o, cons
                         : fa::launch_bwd_dkdv<fa::kElemBf16>(a, d, causal != 0, s));
     if (rc != FA_OK) return rc;
   }
-  if (stages & FA_BWD_DQ)
-    rc = hip_status(f16 ? fa::launch_bwd_dq<fa::kElemF16>(a, d, causal != 0, s)
-                        : fa::launch_bwd_dq<fa::kElemBf16>(a, d, causal != 0, s));
+  if ((stages & FA_BWD_DQ) && !fuse) rc = run_dq();
   return rc;
 }
 

@@ -157,7 +157,30 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
     }
   }
   const float lse2 = a.lse[(int64_t)bh * Nq + qsrc] * kLog2e;
-  const float dlt = a.delta[(int64_t)bh * Nq + qsrc];
+  float dlt;
+  if (a.fuse_delta) {
+    // delta = sum_c dO[row, c] O[row, c] (fp32), formed here from the dO fragments already held
+    // (this lane's half of the row) and the same half of O; the two halves of a row sit in lanes
+    // l and l + 32.  Stored for the dK/dV kernel, which runs after this one.
+    const uint16_t* os = a.o + qoff + (int64_t)qsrc * D + 8 * hh;
+    float acc = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const i32x4 ov = *reinterpret_cast<const i32x4*>(os + 16 * ks);
+      const i32x4 gv = __builtin_bit_cast(i32x4, gf[ks]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x2 o2 = unpack2<E>((uint32_t)ov[i]);
+        const f32x2 g2 = unpack2<E>((uint32_t)gv[i]);
+        acc = fmaf(o2[0], g2[0], acc);
+        acc = fmaf(o2[1], g2[1], acc);
+      }
+    }
+    dlt = acc + __shfl_xor(acc, 32, 64);
+    if (hh == 0 && qrow < Nq) a.delta[(int64_t)bh * Nq + qrow] = dlt;
+  } else {
+    dlt = a.delta[(int64_t)bh * Nq + qsrc];
+  }
 
   int n_kv = (Nk + BC - 1) / BC;
   if (CAUSAL) n_kv = min(n_kv, blocks_through(q0 + BR - 1 + a.coff, BC));

@@ -48,6 +48,7 @@ struct BwdArgs {
   int n_tiles;  // set by each launcher
   float scale;
   float sl2;    // scale * log2(e)
+  int fuse_delta;  // dQ kernel: form delta for its rows (and store it) instead of loading it
 };
 
 // Launchers per element type E (kElemBf16 = 0, kElemF16 = 1 in fa_common.hpp): the kernel
