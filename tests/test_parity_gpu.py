@@ -564,3 +564,55 @@ def test_graph_capture_replays_match_eager(fa):
         for got, want in zip(snapshot(), eager[which]):
             assert torch.equal(got, want), f"replay {rep} differs from the eager result"
         assert torch.isfinite(junk)
+
+
+@pytest.mark.parametrize("d,causal,n", [(128, True, 300), (64, False, 200), (128, False, 129)])
+def test_backward_stage_subsets_agree(fa, d, causal, n):
+    """Every way of running the backward's stages gives the same gradients: the full call (delta
+    formed in the dQ kernel, dQ before dK/dV), the delta stage alone followed by dK/dV + dQ, delta
+    + dK/dV followed by dQ alone, and delta + dQ (fused, without dK/dV) followed by dK/dV alone.
+    delta against the oracle's rowsum(dO o O) within the fp32 accumulation bound; the two fused calls give the
+    same delta bit for bit; dV (independent of delta) bit for bit across all orders; dQ and dK
+    within one bf16 rounding of each other and within the gradient bar of the oracle."""
+    _say("stages", d, causal, n)
+    t = randn_inputs(1, 2, n, d, seed=2100 + n + d)
+    g = _to_dev(t)
+    scale = d ** -0.5
+    o, lse = fa.forward(g["q"], g["k"], g["v"], causal, scale, BETA, 1)
+    A, D, KV, Q = fa.FA_BWD_ALL, fa.FA_BWD_DELTA, fa.FA_BWD_DKDV, fa.FA_BWD_DQ
+
+    def run(seq):
+        dq, dk, dv = (torch.full_like(g["q"], 3.0) for _ in range(3))
+        delta = torch.full_like(lse, 3.0)
+        for st in seq:
+            fa.fa_bwd_ex(g["q"], g["k"], g["v"], o, lse, g["do"], dq, dk, dv, delta, causal, scale,
+                         stages=st)
+        torch.cuda.synchronize()
+        return {"dq": dq.float().cpu().numpy(), "dk": dk.float().cpu().numpy(),
+                "dv": dv.float().cpu().numpy(), "delta": delta.cpu().numpy()}
+
+    runs = {"all": run([A]), "d_then_kvq": run([D, KV | Q]), "dkv_then_q": run([D | KV, Q]),
+            "dq_then_kv": run([D | Q, KV])}
+    ref = runs["all"]
+    assert np.array_equal(ref["delta"], runs["dq_then_kv"]["delta"])
+    for name, r in runs.items():
+        for key in ("dq", "dk", "dv", "delta"):
+            assert np.all(np.isfinite(r[key])), (name, key)
+        assert np.array_equal(r["dv"], ref["dv"]), f"dV differs in {name}"
+        for key in ("dq", "dk"):
+            err = np.abs(r[key] - ref[key])
+            floor = 1e-4 * np.abs(ref[key]).max()
+            assert np.all(err <= 2.0**-7 * np.abs(ref[key]) + floor), f"{key} differs in {name}"
+    for h in range(2):
+        x = {k_: v_[0, h].to(torch.float64).numpy() for k_, v_ in t.items()}
+        oo = o[0, h].double().cpu().numpy()
+        delta_ref = np.sum(x["do"] * oo, axis=1)
+        # fp32 accumulation of d exact products: error within d * 2^-24 * sum |dO o O| per row.
+        bound = d * 2.0**-24 * np.sum(np.abs(x["do"] * oo), axis=1)
+        for name, r in runs.items():
+            err = np.abs(r["delta"][0, h] - delta_ref)
+            assert np.all(err <= bound), f"delta in {name}: worst excess {(err - bound).max():.3e}"
+        br = oracle.backward(x["q"], x["k"], x["v"], x["do"], causal, scale, o=oo,
+                             lse=lse[0, h].double().cpu().numpy())
+        for key, refg in (("dq", br.dq), ("dk", br.dk), ("dv", br.dv)):
+            check_grad(ref[key][0, h], refg, f"{key}[{h}]")
