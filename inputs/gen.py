@@ -115,6 +115,55 @@ def grid_inputs(B, H, N, d, seed, dtype=torch.bfloat16):
     return {"q": q, "k": k, "v": v, "do": do}
 
 
+def tied_maxima_inputs(N, d, seed, dtype=torch.bfloat16, tie_keys=(7, 200), c=2.0, n=None):
+    """One head ([1, 1, N, d]) whose query rows include constructed repeated maxima of chosen sign.
+
+    The first 3n coordinates are split into three blocks P = [0, n), M = [n, 2n), Z = [2n, 3n)
+    (n = d // 3 - 1 by default).  The keys in `tie_keys` hold c on P, c on M and 0 on Z (0 on the
+    remaining coordinates); every other key holds grid values {-0.5, -0.25, 0, 0.25, 0.5} on P,
+    c + 0.5 + {0, 0.25, 0.5} on M and on Z, and N(0, 1) draws elsewhere.  Constructed queries:
+      pos:     a c on P (a in 1/4, 1, 4, 8), 0 elsewhere: the tie keys give the maximum a n c^2
+               and every other key at most a c (n/2) < a n c^2;
+      neg:     -a c on M: the tie keys give -a n c^2, every other key less (its M entries exceed c);
+      zero:    -a c on Z: the tie keys give exactly 0, every other key less;
+      allzero: all coordinates 0: every key gives 0 (the whole row ties).
+    All these dot products are exact in fp32 (entries are multiples of 1/4 with few significant
+    bits), so the row maximum is attained exactly by the tie keys.  Every other query row is
+    N(0, 1/16).  V and dO are N(0, 1).  The constructed rows sit in the first and last 256-row
+    query tiles.  Returns (tensors, rows) with rows a dict of lists of row indices per kind."""
+    n = d // 3 - 1 if n is None else n
+    if 3 * n > d or max(tie_keys) >= N or N < 300:
+        raise ValueError("shape too small for the construction")
+    g = _gen(seed)
+    q = 0.25 * torch.randn((N, d), generator=g)
+    k = torch.randn((N, d), generator=g)
+    v = torch.randn((N, d), generator=g)
+    do = torch.randn((N, d), generator=g)
+    grid_p = torch.tensor((-0.5, -0.25, 0.0, 0.25, 0.5))[torch.randint(0, 5, (N, n), generator=g)]
+    grid_m = torch.tensor((0.0, 0.25, 0.5))[torch.randint(0, 3, (N, n), generator=g)]
+    grid_z = torch.tensor((0.0, 0.25, 0.5))[torch.randint(0, 3, (N, n), generator=g)]
+    k[:, 0:n] = grid_p
+    k[:, n:2 * n] = c + 0.5 + grid_m
+    k[:, 2 * n:3 * n] = c + 0.5 + grid_z
+    for j in tie_keys:
+        k[j] = 0.0
+        k[j, 0:2 * n] = c
+    mults = (0.25, 1.0, 4.0, 8.0)
+    base = (10, N - 40)
+    rows = {"pos": [], "neg": [], "zero": [], "allzero": []}
+    for b0 in base:
+        for i, a in enumerate(mults):
+            for kind, lo, sign, off in (("pos", 0, 1.0, 0), ("neg", n, -1.0, 4), ("zero", 2 * n, -1.0, 8)):
+                r = b0 + off + i
+                q[r] = 0.0
+                q[r, lo:lo + n] = sign * a * c
+                rows[kind].append(r)
+        q[b0 + 12] = 0.0
+        rows["allzero"].append(b0 + 12)
+    t = {"q": q, "k": k, "v": v, "do": do}
+    return {n_: x_.reshape(1, 1, N, d).to(dtype) for n_, x_ in t.items()}, rows
+
+
 def _apply_dup(t):
     """Key 17 := key 3 and queries 0..7 := key 3, so rows 0..7 carry an exact repeated maximum."""
     k, q = t["k"], t["q"]

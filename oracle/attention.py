@@ -55,8 +55,9 @@ CAUSAL_TOP_LEFT = 1
 CAUSAL_BOTTOM_RIGHT = 2
 
 
-def visible(rows, n_keys, causal, n_queries=None):
-    """Boolean [len(rows), n_keys]: whether key j is visible to query row i.
+def visible(rows, n_keys, causal, n_queries=None, keys=None):
+    """Boolean [len(rows), n_keys] (or [len(rows), len(keys)] for a subset `keys` of the key
+    indices): whether key j is visible to query row i.
 
     causal 0 / False: every key.  1 / True (top-left aligned): j <= i.  2 (bottom-right aligned,
     the last query sees every key): j <= i + n_keys - n_queries, so with more queries than keys
@@ -64,10 +65,10 @@ def visible(rows, n_keys, causal, n_queries=None):
     n_queries == n_keys the two alignments coincide.
     """
     rows = np.asarray(rows)
-    keys = np.arange(n_keys)
+    keys = np.arange(n_keys) if keys is None else np.asarray(keys)
     causal = int(causal)
     if causal == CAUSAL_NONE:
-        return np.ones((rows.size, n_keys), dtype=bool)
+        return np.ones((rows.size, keys.size), dtype=bool)
     if causal == CAUSAL_TOP_LEFT:
         off = 0
     elif causal == CAUSAL_BOTTOM_RIGHT:
@@ -117,10 +118,13 @@ def e4m3_round(x):
 P_HAT_FP8_LOG2_SCALE = 8
 
 
-def fp8_p_hat_round(p):
-    """P^ as the FP8 P^ V variant feeds it to the product: e4m3(2^8 P^) / 2^8."""
-    return np.ldexp(e4m3_round(np.ldexp(np.asarray(p, dtype=np.float64), P_HAT_FP8_LOG2_SCALE)),
-                    -P_HAT_FP8_LOG2_SCALE)
+def fp8_p_hat_round(p, extra=0):
+    """P^ as the FP8 P^ V variant feeds it to the product: e4m3(2^(8 + extra) P^) / 2^(8 + extra).
+
+    `extra` (a whole number of binades, broadcast against p; 0 by default) is the variant's own
+    range adjustment for rows whose shift leaves every P^ far below 1 (see tiled_forward)."""
+    e = (P_HAT_FP8_LOG2_SCALE + np.rint(np.asarray(extra, dtype=np.float64))).astype(np.int64)
+    return np.ldexp(e4m3_round(np.ldexp(np.asarray(p, dtype=np.float64), e)), -e)
 
 
 ELEM_ROUND = {"bf16": bf16_round, "f16": fp16_round, "fp8": fp8_p_hat_round}
@@ -180,6 +184,41 @@ class ForwardResult:
     ones: np.ndarray  # [N] count of round(exp(S - m)) == 1.0 over visible keys (int64), rounded
     #                  to the 16-bit element type of the P^ V product
     smin: np.ndarray  # [N] row min of the scaled scores over visible keys
+
+
+def integer_repeat_counts(qi, ki, causal, row_chunk=2048):
+    """Row maximum and repeat count (rowsum(S == rowmax(S)), [BF16-FA] §4.1 / §7.1) of the integer
+    dot products X = qi ki^T over the visible keys, for integer-valued arrays qi [Nq, d] and
+    ki [Nk, d].  Returns (xmax, count) as int64 arrays; a row with no visible key gets count 0.
+
+    The repeat count of the scaled scores S = scale q k^T equals that of X whenever q and k are
+    the integer arrays times a common positive factor (grid inputs: entries multiples of 0.5, so
+    qi = 2q, ki = 2k), since a positive factor preserves order and equality.  The product is
+    formed with a float32 matrix multiply, which is exact here: every partial sum is an integer of
+    magnitude at most d max|qi| max|ki|, checked to be below 2^24.  Rows are processed in chunks
+    of row_chunk to bound memory."""
+    qi = np.asarray(qi)
+    ki = np.asarray(ki)
+    if not (np.array_equal(qi, np.rint(qi)) and np.array_equal(ki, np.rint(ki))):
+        raise ValueError("integer_repeat_counts needs integer-valued inputs")
+    bound = qi.shape[1] * (np.abs(qi).max(initial=0)) * (np.abs(ki).max(initial=0))
+    if bound >= 2**24:
+        raise ValueError("dot products could exceed the exactly representable fp32 integers")
+    n, nk = qi.shape[0], ki.shape[0]
+    q32 = qi.astype(np.float32)
+    k32 = ki.astype(np.float32)
+    xmax = np.zeros(n, dtype=np.int64)
+    count = np.zeros(n, dtype=np.int64)
+    for r0 in range(0, n, row_chunk):
+        rows = np.arange(r0, min(n, r0 + row_chunk))
+        mask = visible(rows, nk, causal, n)
+        x = np.where(mask, q32[rows] @ k32.T, -np.inf)
+        mx = x.max(axis=1, initial=-np.inf)
+        cnt = np.sum(x == mx[:, None], axis=1)
+        live = mx > -np.inf
+        xmax[rows] = np.where(live, mx, 0).astype(np.int64)
+        count[rows] = np.where(live, cnt, 0)
+    return xmax, count
 
 
 def forward_rows(q, k, v, rows, causal, scale, beta=1.25, mode=MODE_STANDARD, elem="bf16"):
@@ -305,57 +344,6 @@ def dq_rows(q, k, v, do, rows, causal, scale, beta=1.25, mode=MODE_STANDARD):
     delta = np.sum(do[rows] * fr.o, axis=1)
     _, ds = _grad_rows(q, k, v, do, rows, causal, scale, fr.lse, delta)
     return scale * (ds @ k), delta
-
-
-def _heads(x):
-    x = np.asarray(x, dtype=np.float64)
-    if x.ndim != 4:
-        raise ValueError("expected a [B, H, N, d] array")
-    return x
-
-
-def forward_bhnd(q, k, v, causal, scale, beta=1.25, mode=MODE_STANDARD, heads=None, row_chunk=1024,
-                 elem="bf16"):
-    """forward() over [B, H, N, d] arrays.  `heads` restricts the work to a list of (b, h) pairs;
-    the other entries of the outputs stay zero.  Returns a dict of stacked arrays."""
-    q, k, v = _heads(q), _heads(k), _heads(v)
-    B, H, N, d = q.shape
-    out = {
-        "o": np.zeros((B, H, N, v.shape[3])),
-        "lse": np.zeros((B, H, N)),
-        "rm": np.zeros((B, H, N)),
-        "rs": np.zeros((B, H, N), dtype=np.int64),
-        "m": np.zeros((B, H, N)),
-        "l": np.zeros((B, H, N)),
-        "ones": np.zeros((B, H, N), dtype=np.int64),
-        "smin": np.zeros((B, H, N)),
-    }
-    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
-    for b, h in pairs:
-        fr = forward(q[b, h], k[b, h], v[b, h], causal, scale, beta, mode, row_chunk, elem)
-        for name in out:
-            out[name][b, h] = getattr(fr, name)
-    return out
-
-
-def backward_bhnd(q, k, v, do, causal, scale, heads=None, row_chunk=1024):
-    """backward() over [B, H, N, d] arrays, restricted to `heads` if given."""
-    q, k, v, do = _heads(q), _heads(k), _heads(v), _heads(do)
-    B, H, N, d = q.shape
-    out = {"dq": np.zeros_like(q), "dk": np.zeros_like(k), "dv": np.zeros_like(v)}
-    out["delta"] = np.zeros((B, H, N))
-    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
-    for b, h in pairs:
-        br = backward(q[b, h], k[b, h], v[b, h], do[b, h], causal, scale, row_chunk=row_chunk)
-        for name in out:
-            out[name][b, h] = getattr(br, name)
-    return out
-
-
-def flops_forward(B, H, N, d, causal):
-    """The FlashAttention flop convention: 4 B H N^2 d, halved when causal."""
-    f = 4.0 * B * H * N * N * d
-    return f / 2 if causal else f
 
 
 def exact_causal_pairs(N):

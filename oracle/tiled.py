@@ -53,7 +53,13 @@ def tiled_forward(q, k, v, causal, scale, beta=1.25, mode=0, bc=64, order=None, 
     pv="fp8" is the FP8 P^ V variant ([BF16-FA] §6.1 names FP8 as the next lower precision): the
     block's product P^ V takes P^ rounded by fp8_p_hat_round and V rounded by fp8_v_block (one
     dynamic scale per key block of width bc); the row sum l, the shift m and the LSE are the
-    unrounded ones, and O = acc / l as before.
+    unrounded ones, and O = acc / l as before.  Where the shift lies more than 5 binades below the
+    running maximum (g = (m - r) / ln 2 > 5), every P^ of the row is below 2^-5 and e4m3(2^8 P^)
+    would lose it to the subnormals and to zero; the variant then rounds P^ as
+    e4m3(2^(8 + k) P^) / 2^(8 + k) with k = floor(g) - 5, which puts the row's largest value in
+    (2^2, 2^3] before rounding.  (The variant's own design: the pages fix no FP8 scaling.  A kernel
+    evaluates g in fp32, so for g within rounding of a whole number its k can differ by one; the
+    rounding error stays within the same bound.)
     """
     if pv not in ("exact", "fp8"):
         raise ValueError(f"pv must be 'exact' or 'fp8', got {pv!r}")
@@ -89,7 +95,9 @@ def tiled_forward(q, k, v, causal, scale, beta=1.25, mode=0, bc=64, order=None, 
         p_hat = np.where(mask, np.exp(s - np.where(live, m_new, 0.0)[:, None]), 0.0)
         l = alpha * l + p_hat.sum(axis=1)
         if pv == "fp8":
-            acc = alpha[:, None] * acc + fp8_p_hat_round(p_hat) @ fp8_v_block(v[k0:k1])[0]
+            gap = np.where(live, (np.where(live, m_new, 0.0) - np.where(live, r, 0.0)) / np.log(2.0), 0.0)
+            extra = np.where(gap > 5.0, np.floor(gap) - 5.0, 0.0)
+            acc = alpha[:, None] * acc + fp8_p_hat_round(p_hat, extra[:, None]) @ fp8_v_block(v[k0:k1])[0]
         else:
             acc = alpha[:, None] * acc + p_hat @ v[k0:k1]
         ones += np.sum((ELEM_ROUND[elem](p_hat) == 1.0) & mask, axis=1)
@@ -105,7 +113,9 @@ def tiled_ones(q, k, causal, scale, beta=1.25, mode=0, bc=64, order=None, elem="
     """Per-row count of exact-1.0 bf16 unnormalised probabilities under block-wise processing.
 
     Same recurrence as tiled_forward without V; used where only the count is needed (large
-    heads), to save the P^ V product.
+    heads), to save the P^ V product.  A block invisible to a row leaves that row's state
+    unchanged (as in tiled_forward), so each block is evaluated only for the rows that see at
+    least one of its keys.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -114,21 +124,23 @@ def tiled_ones(q, k, causal, scale, beta=1.25, mode=0, bc=64, order=None, elem="
     n_blocks = -(-n_keys // bc)
     if order is None:
         order = range(n_blocks)
-    rows = np.arange(n)
+    rows_all = np.arange(n)
     r = np.full(n, -np.inf)
     c = np.zeros(n, dtype=np.int64)
     ones = np.zeros(n, dtype=np.int64)
     for j in order:
         k0, k1 = j * bc, min(n_keys, (j + 1) * bc)
-        mask = visible(rows, n_keys, causal, n)[:, k0:k1]
-        s = np.where(mask, scale * (q @ k[k0:k1].T), -np.inf)
+        mask = visible(rows_all, n_keys, causal, n, keys=np.arange(k0, k1))
+        rows = np.nonzero(mask.any(axis=1))[0]
+        mask = mask[rows]
+        s = np.where(mask, scale * (q[rows] @ k[k0:k1].T), -np.inf)
         tm = np.max(s, axis=1)
         tc = np.sum((s == tm[:, None]) & mask, axis=1)
-        r_new = np.maximum(r, tm)
-        c = np.where(tm == r_new, tc, 0) + np.where(r == r_new, c, 0)
-        r = r_new
-        live = np.isfinite(r)
-        m = stable_shift(np.where(live, r, 0.0), c, beta, mode)
+        r_new = np.maximum(r[rows], tm)
+        c[rows] = np.where(tm == r_new, tc, 0) + np.where(r[rows] == r_new, c[rows], 0)
+        r[rows] = r_new
+        live = np.isfinite(r_new)
+        m = stable_shift(np.where(live, r_new, 0.0), c[rows], beta, mode)
         p_hat = np.where(mask, np.exp(s - m[:, None]), 0.0)
-        ones += np.sum((ELEM_ROUND[elem](p_hat) == 1.0) & mask, axis=1)
+        ones[rows] += np.sum((ELEM_ROUND[elem](p_hat) == 1.0) & mask, axis=1)
     return ones

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from inputs import make_inputs, grid_inputs
+from inputs import make_inputs, grid_inputs, rect_inputs, tied_maxima_inputs
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 BETA = 1.25
@@ -349,6 +349,60 @@ def test_dupcount_by_integer_arithmetic():
             fr = oracle.forward(q, k, q, causal, 0.0883883461356163, BETA, 1)
             assert np.array_equal(fr.rs, rs)
             assert rs.max() > 1  # the grid really produces ties
+
+
+@pytest.mark.parametrize("causal", [0, 1, 2])
+@pytest.mark.parametrize("nq,nk", [(333, 333), (96, 416), (416, 96)])
+def test_integer_repeat_counts_match_the_scaled_scores(causal, nq, nk):
+    t = rect_inputs(1, 1, nq, nk, 64, seed=nq + 7 * nk + causal, grid=True)
+    q, k = _np(t["q"][0, 0]), _np(t["k"][0, 0])
+    xmax, cnt = oracle.integer_repeat_counts(2 * q, 2 * k, causal, row_chunk=100)
+    s = oracle.scaled_scores(q, k, 0.0883883461356163, oracle.visible(np.arange(nq), nk, causal, nq))
+    rm, rs = oracle.row_max_and_repeats(s)
+    assert np.array_equal(cnt, rs)
+    live = rs > 0
+    assert np.array_equal(xmax[live] * 0.25 * 0.0883883461356163, rm[live])
+    assert rs.max() > 1
+
+
+def test_integer_repeat_counts_brute_force_and_guards():
+    rng = np.random.default_rng(5)
+    qi = rng.integers(-2, 3, (9, 5)).astype(np.float64)
+    ki = rng.integers(-2, 3, (11, 5)).astype(np.float64)
+    for causal in (0, 1, 2):
+        xmax, cnt = oracle.integer_repeat_counts(qi, ki, causal, row_chunk=4)
+        off = {0: None, 1: 0, 2: 11 - 9}[causal]
+        for i in range(9):
+            vals = [int(sum(qi[i, t] * ki[j, t] for t in range(5))) for j in range(11)
+                    if off is None or j <= i + off]
+            if not vals:
+                assert cnt[i] == 0
+                continue
+            assert xmax[i] == max(vals) and cnt[i] == vals.count(max(vals))
+    with pytest.raises(ValueError):
+        oracle.integer_repeat_counts(qi + 0.5, ki, 0)
+    with pytest.raises(ValueError):
+        oracle.integer_repeat_counts(qi * 4096, ki * 4096, 0)
+
+
+def test_tied_maxima_construction():
+    """The constructed rows attain their maximum exactly at the two tie keys, with the sign asked
+    for; the rule then gives beta rm, 0 and 0 (closed form of [BF16-FA] §4.1)."""
+    for d in (64, 128):
+        t, rows = tied_maxima_inputs(300, d, seed=3 + d)
+        x = _head(t)
+        scale = 0.125 if d == 64 else 0.0883883461356163
+        fr = oracle.forward(x["q"], x["k"], x["v"], False, scale, 1.5, 1)
+        s = scale * x["q"] @ x["k"].T
+        for kind, rr in rows.items():
+            if kind == "allzero":
+                assert np.all(s[rr] == 0.0) and np.all(fr.rs[rr] == 300)
+                continue
+            assert np.all(np.argsort(-s[rr], axis=1, kind="stable")[:, :2] == [7, 200])
+            assert np.all(fr.rs[rr] == 2)
+            sign = {"pos": 1, "neg": -1, "zero": 0}[kind]
+            assert np.all(np.sign(fr.rm[rr]) == sign)
+            assert np.all(fr.m[rr] == (1.5 * fr.rm[rr] if kind == "pos" else 0.0))
 
 
 def test_dupcount_config1_construction():
@@ -780,6 +834,38 @@ def test_fp8_pv_tiled_forward_brute_force(causal):
     got = oracle.tiled_forward(q, k, v, causal, 0.35, mode=0, bc=128, pv="fp8")["o"]
     want = _brute_fp8_forward(q, k, v, causal, 0.35)
     assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def _fp8_bound(x, fr, scale, n):
+    mask = np.ones((n, n), dtype=bool)
+    p = oracle.probabilities(x["q"], x["k"], scale, fr.lse, mask)
+    return (p @ np.abs(x["v"])) * (2.0**-4 + 2.0**-4 + 2.0**-8) + 2.0**-14 * np.abs(x["v"]).max()
+
+
+def test_fp8_pv_replay_keeps_rows_with_large_shifts(monkeypatch):
+    """Rows whose repeated maximum is +-58 or +-116 (tied_maxima_inputs, d = 128): under the rule
+    every P^ of the row is at most e^{-(beta-1) rm} or e^{rm}, so e4m3(2^8 P^) would be 0.  With the
+    variant's range adjustment the replay stays within the E4M3 rounding bound of the exact O; a
+    replay that drops the adjustment (planted) returns O = 0 there and fails the same bound."""
+    t, rows = tied_maxima_inputs(300, 128, seed=2400)
+    x = _head(t)
+    scale = 0.0883883461356163
+    big = [r for r in rows["pos"] + rows["neg"]]
+    for mode in (1, 2):
+        fr = oracle.forward(x["q"], x["k"], x["v"], False, scale, BETA, mode)
+        big = [r for r in rows["pos"] + rows["neg"] if abs(fr.rm[r]) >= 40.0]
+        assert len(big) == 8 and np.all(np.exp(fr.rm[big] - fr.m[big]) < 2.0**-18)  # 2^8 P^ < 2^-10
+        f8 = oracle.tiled_forward(x["q"], x["k"], x["v"], False, scale, BETA, mode, bc=128, pv="fp8")
+        bound = _fp8_bound(x, fr, scale, 300)
+        err = np.abs(f8["o"] - fr.o)
+        assert np.all(err[big] <= bound[big])
+        assert np.abs(fr.o[big]).max() > 0.5
+    import oracle.tiled as tiled
+    plain = tiled.fp8_p_hat_round
+    monkeypatch.setattr(tiled, "fp8_p_hat_round", lambda p, extra=0: plain(p))
+    f8 = oracle.tiled_forward(x["q"], x["k"], x["v"], False, scale, BETA, 2, bc=128, pv="fp8")
+    assert np.all(f8["o"][big] == 0.0)
+    assert not np.all(np.abs(f8["o"] - fr.o)[big] <= _fp8_bound(x, fr, scale, 300)[big])
 
 
 @pytest.mark.parametrize("mode", [0, 1, 2])
