@@ -173,8 +173,13 @@ int fa_bwd_qk(const void* q, const void* k, const void* v, const void* o, const 
  * exponent is shifted first.  Every product still accumulates in fp32 and the softmax runs in fp32;
  * with either element type the unnormalised probabilities P^ = exp(S - m) are at most 1 after the
  * shift (P^ = 1 at a maximum only where m equals it), so they and P are in range, and they are
- * rounded (to nearest even) to the element type for the P^ V, P^T dO and dS products.  The
- * exact-1.0 count (ones) compares the element type's 1.0. */
+ * rounded (to nearest even) to the element type for the P^ V, P^T dO and dS products.  Where the
+ * rule's shift leaves the largest P^ of a row below 2^-13 (a repeated maximum rm with
+ * (beta - 1) rm > 13 ln 2, or a negative one below -13 ln 2, shifted to 0), the forward takes its
+ * exponentials against m lowered by a whole number of binades so that the largest value lands in
+ * (2^-14, 2^-13]: the common power of two cancels in O / l and in LSE, the rounding is unchanged
+ * in relative terms, and P^ neither goes subnormal in fp16 nor rounds to 1.0.  The exact-1.0 count
+ * (ones) compares the element type's 1.0. */
 #define FA_ELEM_BF16 0
 #define FA_ELEM_F16 1
 
@@ -193,6 +198,22 @@ int fa_bwd_elem(const void* q, const void* k, const void* v, const void* o, cons
                 int B, int H, int Nq, int Nk, int d, int causal, float scale, float beta,
                 int stable_flag, int stages, int elem, void* stream);
 
+/* fa_fwd_elem with one more per-row output (NULL allowed):
+ *   mshift[b,h,i] = the shift m of the repeated-maximum rule after the last key block, fp32, in
+ *                   the natural-log units of the scaled scores S: with rm the row maximum of S,
+ *                   m = beta * rm when rm > 0 and rm repeats, m = 0 when rm < 0 and rm repeats, and
+ *                   m = rm otherwise (the ijyty.com article §4.1 and its closed form in §3.2;
+ *                   "為什么BF16的FlashAttention會把訓練「炸掉」？", web578.cn, mechanism 2).  With
+ *                   stable_flag 0, m = rm; with 2 every row counts as repeating.  The value is the
+ *                   kernel's own (formed from its running maximum and repeat test as each key block
+ *                   forms it), -inf for a row that sees no key.  Writing it does not select the
+ *                   diagnostics variant: with only mshift requested, the kernel that fa_fwd runs writes it.
+ * fa_fwd_elem(...) == fa_fwd_diag(..., mshift = NULL, ...).  Errors as fa_fwd_elem. */
+int fa_fwd_diag(const void* q, const void* k, const void* v, void* o, float* lse,
+                int32_t* dupcnt, int32_t* ones, float* smin, float* smax, float* mshift,
+                int B, int H, int Nq, int Nk, int d, int causal, float scale, float beta,
+                int stable_flag, int flags, int elem, void* stream);
+
 /* Forward pass with the P^ V product in FP8 (OCP E4M3, the "e4m3fn" encoding, largest value 448):
  * the lower-precision extension the ijyty.com article §6.1 names, with dynamic scaling.  Tensors,
  * shapes, diagnostics, causal alignments and errors as fa_fwd_qk (bf16 q, k, v, o); the scores
@@ -201,7 +222,9 @@ int fa_bwd_elem(const void* q, const void* k, const void* v, const void* o, cons
  *   - V, per head and block of 128 consecutive keys: s = amax |V_block| / 448 (fp32; s = 1 for an
  *     all-zero block), each value stored as E4M3(v * (1 / s)) and standing for that value times s;
  *   - P^ = exp(S - m) <= 1, as E4M3(2^8 P^) (so that P^ down to 2^-14 keeps 4 significant bits),
- *     standing for that value times 2^-8.
+ *     standing for that value times 2^-8.  Where the rule's shift leaves the largest P^ of the row
+ *     below 2^-5 (see FA_ELEM_F16), P^ is first multiplied by the power of two 2^k that brings that
+ *     largest value into (2^-6, 2^-5], and the product carries 2^-k (cancelling in O / l).
  * O = sum over blocks of the rescaled products, divided by the unrounded l.  ones counts the P^
  * whose rounded value is exactly 1.0 (2^8 P^ rounds to 256, i.e. P^ >= 0.96875).  The key blocks
  * of this forward are 128 keys wide whether or not it is causal.
@@ -225,22 +248,6 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  * causal flag (any non-zero alignment counts as causal; 0 if d is not supported): the
  * granularity at which the running maximum, repeat count and shift change. */
 int fa_fwd_kv_block(int d, int causal);
-
-/* Measurement helper, not part of the attention path: runs n_workgroups workgroups of 256
- * threads, each wave issuing iters * 32 dense bf16 32x32x16 MFMAs (2^15 flop each) on register
- * operands, and writes one float per thread to out (caller-owned device memory of
- * n_workgroups * 256 floats, 4-byte aligned; the values are meaningless).  Timing it gives the
- * MFMA rate the GPU sustains, reported beside the published peak.  Errors: FA_ERR_NULL,
- * FA_ERR_PARAM (n_workgroups outside 1 .. 2^20 or iters < 1), FA_ERR_ALIGN, FA_ERR_HIP. */
-int fa_probe_mfma_peak(float* out, int n_workgroups, int iters, void* stream);
-
-/* Measurement helper, not part of the attention path: runs n_workgroups workgroups of 256
- * threads holding 64 KiB of LDS each (two per CU), each wave reading iters * 16 KiB of LDS with
- * conflict-free 16-byte reads, and writes one float per thread to out (caller-owned device
- * memory of n_workgroups * 256 floats, 4-byte aligned; the values are meaningless).  Timing it
- * gives the LDS read bandwidth the GPU sustains, the ceiling of the kernels' LDS operand reads.
- * Errors: as fa_probe_mfma_peak. */
-int fa_probe_lds_read(float* out, int n_workgroups, int iters, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* fa_status_str(int status);

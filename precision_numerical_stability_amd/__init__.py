@@ -39,7 +39,7 @@ __all__ = [
     "fa_fwd", "fa_fwd_ex", "fa_fwd_stats", "fa_fwd_qk", "fa_fwd_elem", "FA_FWD_COMPENSATED_SUM",
     "fa_bwd", "fa_bwd_ex", "fa_bwd_qk", "fa_bwd_elem", "FA_ELEM_BF16", "FA_ELEM_F16",
     "fa_fwd_fp8pv", "fa_fwd_fp8pv_workspace_bytes", "forward_fp8pv",
-    "fa_bwd_workspace_bytes", "fa_fwd_kv_block", "fa_probe_mfma_peak", "fa_probe_lds_read",
+    "fa_bwd_workspace_bytes", "fa_fwd_kv_block", "fa_fwd_diag",
     "FA_CAUSAL_NONE", "FA_CAUSAL_TOP_LEFT", "FA_CAUSAL_BOTTOM_RIGHT", "fa_status_str",
     "fa_last_hip_error", "FaError", "forward", "backward", "attention", "STANDARD", "TIE_RULE",
     "TIE_ANTICIPATE", "DEFAULT_BETA", "library_path",
@@ -73,30 +73,6 @@ def fa_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
 
 def fa_fwd_kv_block(d: int, causal: bool) -> int:
     return int(_lib.fa_fwd_kv_block(d, int(bool(causal))))
-
-
-def fa_probe_mfma_peak(out, n_workgroups: int, iters: int, stream=None) -> None:
-    """Measurement helper (not part of the attention path): n_workgroups x 256 threads of pure
-    bf16 MFMA work, iters * 32 MFMAs of 2^15 flop per wave; out is a float32 CUDA tensor of at
-    least n_workgroups * 256 elements."""
-    if out.dtype != torch.float32 or not out.is_cuda or out.numel() < n_workgroups * 256:
-        raise ValueError("out must be a float32 CUDA tensor of n_workgroups * 256 elements")
-    st = _stream_handle(out.device, stream)
-    rc = _lib.fa_probe_mfma_peak(_ptr(out), int(n_workgroups), int(iters), st)
-    if rc != FA_OK:
-        raise FaError(rc)
-
-
-def fa_probe_lds_read(out, n_workgroups: int, iters: int, stream=None) -> None:
-    """Measurement helper (not part of the attention path): n_workgroups x 256 threads, each wave
-    reading iters * 16 KiB of LDS in conflict-free 16-byte reads; out is a float32 CUDA tensor of
-    at least n_workgroups * 256 elements."""
-    if out.dtype != torch.float32 or not out.is_cuda or out.numel() < n_workgroups * 256:
-        raise ValueError("out must be a float32 CUDA tensor of n_workgroups * 256 elements")
-    st = _stream_handle(out.device, stream)
-    rc = _lib.fa_probe_lds_read(_ptr(out), int(n_workgroups), int(iters), st)
-    if rc != FA_OK:
-        raise FaError(rc)
 
 
 def _ptr(t):
@@ -211,6 +187,28 @@ def fa_fwd_elem(q, k, v, o, lse, dupcnt, ones, smin, smax, causal, scale, beta, 
     _raise(st)
 
 
+def fa_fwd_diag(q, k, v, o, lse, dupcnt, ones, smin, smax, mshift, causal, scale, beta, stable_flag,
+                flags=0, stream=None):
+    """Call fa_fwd_diag on torch tensors: as fa_fwd_elem, plus mshift [B,H,Nq] fp32 or None (the
+    per-row shift of the repeated-maximum rule after the last key block)."""
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    elem = _elem(q, "q")
+    for name, t, n in (("q", q, Nq), ("o", o, Nq), ("k", k, Nk), ("v", v, Nk)):
+        _check(t, name, q.dtype, (B, H, n, d))
+    _check(lse, "lse", torch.float32, (B, H, Nq))
+    for name, t, dt in (("dupcnt", dupcnt, torch.int32), ("ones", ones, torch.int32),
+                        ("smin", smin, torch.float32), ("smax", smax, torch.float32),
+                        ("mshift", mshift, torch.float32)):
+        if t is not None:
+            _check(t, name, dt, (B, H, Nq))
+    st = _lib.fa_fwd_diag(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dupcnt), _ptr(ones),
+                          _ptr(smin), _ptr(smax), _ptr(mshift), B, H, Nq, Nk, d, int(causal),
+                          float(scale), float(beta), int(stable_flag), int(flags), elem,
+                          _stream_handle(q.device, stream))
+    _raise(st)
+
+
 def fa_fwd_fp8pv_workspace_bytes(B: int, H: int, Nk: int, d: int) -> int:
     return int(_lib.fa_fwd_fp8pv_workspace_bytes(B, H, Nk, d))
 
@@ -315,12 +313,12 @@ def _default_scale(d):
 
 
 def forward(q, k, v, causal=False, scale=None, beta=DEFAULT_BETA, stable_flag=TIE_RULE,
-            stats=False, monitor=False, compensated_sum=False, stream=None):
-    """Allocate outputs and run the forward (fa_fwd_elem: bfloat16 or float16 tensors; k and v may
+            stats=False, monitor=False, compensated_sum=False, shift=False, stream=None):
+    """Allocate outputs and run the forward (fa_fwd_diag: bfloat16 or float16 tensors; k and v may
     hold a different number of keys than q has queries; causal 0/False, 1/True (top-left) or 2
     (bottom-right)).  Returns
-    (o, lse), plus (dupcnt, ones) with stats=True, plus (smin, smax) with monitor=True.
-    compensated_sum selects the Kahan row sum."""
+    (o, lse), plus (dupcnt, ones) with stats=True, plus (smin, smax) with monitor=True, plus the
+    per-row shift m with shift=True.  compensated_sum selects the Kahan row sum."""
     B, H, N, d = q.shape
     scale = _default_scale(d) if scale is None else scale
     o = torch.empty_like(q)
@@ -332,14 +330,17 @@ def forward(q, k, v, causal=False, scale=None, beta=DEFAULT_BETA, stable_flag=TI
     if monitor:
         smin = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
         smax = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    msh = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if shift else None
     flags = FA_FWD_COMPENSATED_SUM if compensated_sum else 0
-    fa_fwd_elem(q, k, v, o, lse, dup, ones, smin, smax, int(causal), scale, beta, stable_flag, flags,
-                stream)
+    fa_fwd_diag(q, k, v, o, lse, dup, ones, smin, smax, msh, int(causal), scale, beta, stable_flag,
+                flags, stream)
     out = (o, lse)
     if stats:
         out += (dup, ones)
     if monitor:
         out += (smin, smax)
+    if shift:
+        out += (msh,)
     return out
 
 

@@ -42,6 +42,7 @@ SIGNATURES = {
     "fa_fwd_qk": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _I, _P]),
     "fa_bwd_qk": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _I, _P]),
     "fa_fwd_elem": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _I, _I, _P]),
+    "fa_fwd_diag": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _I, _I, _P]),
     "fa_bwd_elem": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _I, _I, _P]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _I, _P]),
     "fa_bwd_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _I, _I, _P]),
@@ -49,8 +50,6 @@ SIGNATURES = {
     "fa_fwd_fp8pv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _I, _P]),
     "fa_fwd_fp8pv_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "fa_fwd_kv_block": (_I, [_I, _I]),
-    "fa_probe_mfma_peak": (_I, [_P, _I, _I, _P]),
-    "fa_probe_lds_read": (_I, [_P, _I, _I, _P]),
     "fa_status_str": (ctypes.c_char_p, [_I]),
     "fa_last_hip_error": (_I, []),
 }

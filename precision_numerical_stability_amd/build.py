@@ -25,7 +25,6 @@ UNITS = (
     ("fa_bwd.hip", "fa_bwd_bf16", ("-DFA_ELEM=0",)),
     ("fa_bwd.hip", "fa_bwd_f16", ("-DFA_ELEM=1",)),
     ("fa_api.cpp", "fa_api", ()),
-    ("fa_probe.hip", "fa_probe", ()),
 )
 SOURCES = tuple(sorted({u[0] for u in UNITS}))
 ARCH = "gfx950"

@@ -52,7 +52,7 @@ size_t fp8pv_v8_bytes(int64_t bh, int Nk, int d) { return size_t(bh) * size_t((N
 // The forward entry points share this body; elem is FA_ELEM_BF16, FA_ELEM_F16 or -1 for the FP8
 // P^ V variant (bf16 tensors), which also takes the workspace.
 int fwd_body(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* dupcnt, int32_t* ones,
-             float* smin, float* smax, void* workspace, int B, int H, int Nq, int Nk, int d, int causal,
+             float* smin, float* smax, float* mshift, void* workspace, int B, int H, int Nq, int Nk, int d, int causal,
              float scale, float beta, int stable_flag, int flags, int elem, void* stream) {
   const bool fp8pv = elem < 0;
   const int st = check_common(B, H, Nq, Nk, d, causal, scale, beta, stable_flag);
@@ -64,7 +64,7 @@ int fwd_body(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (Nk > 0 && (!k || !v)) return FA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return FA_ERR_ALIGN;
   if (!aligned(lse, 4) || (dupcnt && !aligned(dupcnt, 4)) || (ones && !aligned(ones, 4))) return FA_ERR_ALIGN;
-  if ((smin && !aligned(smin, 4)) || (smax && !aligned(smax, 4))) return FA_ERR_ALIGN;
+  if ((smin && !aligned(smin, 4)) || (smax && !aligned(smax, 4)) || (mshift && !aligned(mshift, 4))) return FA_ERR_ALIGN;
   if (fp8pv && Nk > 0 && !workspace) return FA_ERR_NULL;
   if (fp8pv && !aligned(workspace, 16)) return FA_ERR_ALIGN;
 
@@ -78,6 +78,7 @@ int fwd_body(const void* q, const void* k, const void* v, void* o, float* lse, i
   a.ones = ones;
   a.smin = smin;
   a.smax = smax;
+  a.mshift = mshift;
   a.BH = B * H;
   a.Nq = Nq;
   a.Nk = Nk;
@@ -107,16 +108,23 @@ int fwd_body(const void* q, const void* k, const void* v, void* o, float* lse, i
 
 extern "C" {
 
-int fa_fwd_elem(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* dupcnt,
-                int32_t* ones, float* smin, float* smax, int B, int H, int Nq, int Nk, int d, int causal,
-                float scale, float beta, int stable_flag, int flags, int elem, void* stream) {
+int fa_fwd_diag(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* dupcnt,
+                int32_t* ones, float* smin, float* smax, float* mshift, int B, int H, int Nq, int Nk, int d,
+                int causal, float scale, float beta, int stable_flag, int flags, int elem, void* stream) {
   if (elem != FA_ELEM_BF16 && elem != FA_ELEM_F16) {
     // parameters are checked in the documented order: shapes and scalars first
     const int st = check_common(B, H, Nq, Nk, d, causal, scale, beta, stable_flag);
     return st != FA_OK ? st : FA_ERR_PARAM;
   }
-  return fwd_body(q, k, v, o, lse, dupcnt, ones, smin, smax, nullptr, B, H, Nq, Nk, d, causal, scale, beta,
-                  stable_flag, flags, elem, stream);
+  return fwd_body(q, k, v, o, lse, dupcnt, ones, smin, smax, mshift, nullptr, B, H, Nq, Nk, d, causal, scale,
+                  beta, stable_flag, flags, elem, stream);
+}
+
+int fa_fwd_elem(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* dupcnt,
+                int32_t* ones, float* smin, float* smax, int B, int H, int Nq, int Nk, int d, int causal,
+                float scale, float beta, int stable_flag, int flags, int elem, void* stream) {
+  return fa_fwd_diag(q, k, v, o, lse, dupcnt, ones, smin, smax, nullptr, B, H, Nq, Nk, d, causal, scale, beta,
+                     stable_flag, flags, elem, stream);
 }
 
 size_t fa_fwd_fp8pv_workspace_bytes(int B, int H, int Nk, int d) {
@@ -128,8 +136,8 @@ size_t fa_fwd_fp8pv_workspace_bytes(int B, int H, int Nk, int d) {
 int fa_fwd_fp8pv(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* dupcnt,
                  int32_t* ones, float* smin, float* smax, void* workspace, int B, int H, int Nq, int Nk, int d,
                  int causal, float scale, float beta, int stable_flag, int flags, void* stream) {
-  return fwd_body(q, k, v, o, lse, dupcnt, ones, smin, smax, workspace, B, H, Nq, Nk, d, causal, scale, beta,
-                  stable_flag, flags, -1, stream);
+  return fwd_body(q, k, v, o, lse, dupcnt, ones, smin, smax, nullptr, workspace, B, H, Nq, Nk, d, causal, scale,
+                  beta, stable_flag, flags, -1, stream);
 }
 
 int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* dupcnt,
@@ -251,20 +259,6 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
 }
 
 int fa_fwd_kv_block(int d, int causal) { return fa::fwd_kv_block(d, causal != 0); }
-
-int fa_probe_mfma_peak(float* out, int n_workgroups, int iters, void* stream) {
-  if (!out) return FA_ERR_NULL;
-  if (n_workgroups < 1 || iters < 1 || n_workgroups > (1 << 20)) return FA_ERR_PARAM;
-  if (!aligned(out, 4)) return FA_ERR_ALIGN;
-  return hip_status(fa::launch_mfma_peak(out, n_workgroups, iters, static_cast<hipStream_t>(stream)));
-}
-
-int fa_probe_lds_read(float* out, int n_workgroups, int iters, void* stream) {
-  if (!out) return FA_ERR_NULL;
-  if (n_workgroups < 1 || iters < 1 || n_workgroups > (1 << 20)) return FA_ERR_PARAM;
-  if (!aligned(out, 4)) return FA_ERR_ALIGN;
-  return hip_status(fa::launch_lds_read(out, n_workgroups, iters, static_cast<hipStream_t>(stream)));
-}
 
 const char* fa_status_str(int status) {
   switch (status) {

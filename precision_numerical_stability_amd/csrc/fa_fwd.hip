@@ -60,6 +60,36 @@ struct RowState {
   float vs;       // FP8 P^ V: scale of the V block last added (O is held in units of vs / 2^8)
 };
 
+// The shift m of the repeated-maximum rule, in log2 units of the scaled score, from the running
+// state: m = beta r when the running maximum r is positive and repeats, 0 when it is negative and
+// repeats, r otherwise (mode 2 takes every row as repeating).  Mode 1 knows whether r repeats from
+// the two largest scores (TOP2) or from the exact count (the diagnostics variant).
+template <int MODE, bool TOP2>
+__device__ __forceinline__ float page_shift(const RowState& rs, float sl2, float beta) {
+  const float r2 = rs.run_max * sl2;
+  if (MODE == 0) return r2;
+  const bool rep = (MODE == 2) || (TOP2 ? (rs.run_m2 == rs.run_max) : (rs.run_cnt > 1));
+  return (rep && r2 > 0.f) ? beta * r2 : ((rep && r2 < 0.f) ? 0.f : r2);
+}
+
+// The shift the exponentials are taken against.  Under the rule's shift the largest P^ of a row is
+// 2^(r - m), far below 1 when m - r is large (a large repeated maximum, or a negative one shifted
+// to 0), and the 16-bit (or E4M3) rounding of P^ for the V product would go subnormal and then to
+// zero, silently zeroing O.  When m - r exceeds kT, the exponent is taken against m minus a whole
+// number of binades, so the largest P^ lands in (2^-(kT+1), 2^-kT]: O, l and the rescale factors
+// all carry the same power of two, which cancels in O / l and is the shift's own part of the saved
+// logsumexp (LSE = shift + log l).  The rounding of P^ is unchanged in relative terms, and P^ stays
+// well below 1, so no exact 1.0 appears.  kT = 13 keeps 16-bit P^ in fp16's normal range (down to
+// 2^-14); the FP8 variant forms 2^8 P^ and takes kT = 5 (largest value in (4, 8], E4M3 normal from
+// 2^-6).  A lane that has seen no key yet (r = -inf) keeps the rule's value.
+template <bool FP8>
+__device__ __forceinline__ float exponent_shift(float m2, float r2) {
+  constexpr float kT = FP8 ? 5.f : 13.f;
+  const float gap = m2 - r2;
+  const float ofs = (gap > kT && gap < 1048576.f) ? floorf(gap) - kT : 0.f;
+  return m2 - ofs;
+}
+
 template <int E, int D, bool CAUSAL, int MODE, bool STATS, bool KAHAN>
 __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   constexpr int BC = fwd_bc<E, CAUSAL>(), BR = kFwdBr, KS = D / 16, DT = D / 32, KB = BC / 32;
@@ -352,12 +382,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
     // Shift for this block (log2 units).  The sign test is unchanged by the positive factor
     // scale * log2(e), and the rule is positively homogeneous, so applying it here equals
     // applying it to the natural-log scores.
-    const float r2 = rs.run_max * a.sl2;
-    float m2_new = r2;
-    if (MODE != 0) {
-      const bool rep = (MODE == 2) || (TOP2 ? (rs.run_m2 == rs.run_max) : (rs.run_cnt > 1));
-      m2_new = (rep && r2 > 0.f) ? a.beta * r2 : ((rep && r2 < 0.f) ? 0.f : r2);
-    }
+    float m2_new = rs.run_max * a.sl2;
+    if (MODE != 0) m2_new = exponent_shift<FP8>(page_shift<MODE, TOP2>(rs, a.sl2, a.beta), m2_new);
     const float alpha = fast_exp2(rs.m2 - m2_new);
     rs.m2 = m2_new;
     // The factor O is rescaled by.  FP8: O is held in units of this block's V scale over 2^8, so
@@ -484,6 +510,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
     if (hh == 0) {
       const int64_t ri = (int64_t)bh * Nq + qrow;
       a.lse[ri] = empty ? -INFINITY : (rs.m2 + __log2f(ltot) - (FP8 ? 8.f : 0.f)) * kLn2;
+      // The rule's shift after the last key block (natural-log units), recomputed from the final
+      // running state exactly as the last vector phase formed it.
+      if (a.mshift) a.mshift[ri] = empty ? -INFINITY : page_shift<MODE, TOP2>(rs, a.sl2, a.beta) * kLn2;
       if (STATS) {
         if (a.dupcnt) a.dupcnt[ri] = empty ? 0 : rs.run_cnt;
         if (a.ones) a.ones[ri] = empty ? 0 : ones_tot;

@@ -17,6 +17,7 @@ struct FwdArgs {
   int32_t* ones;    // may be null
   float* smin;      // may be null: per-row min of the scaled visible scores
   float* smax;      // may be null: per-row max of the scaled visible scores
+  float* mshift;    // may be null: per-row shift of the repeated-maximum rule (natural log)
   int BH;           // B * H
   int Nq;           // queries per head
   int Nk;           // keys per head
@@ -65,8 +66,6 @@ int fwd_kv_block(int d, bool causal);
 // FP8 P^ V: quantise V ([BH, Nk, d] bf16) into v8 ([BH, ceil(Nk / 128), d, 128] bytes) and
 // vscale ([BH, ceil(Nk / 128)] fp32).  Defined in the FA_ELEM = 2 instance of fa_fwd.hip.
 hipError_t launch_v8_pack(const uint16_t* v, uint8_t* v8, float* vscale, int BH, int Nk, int d, hipStream_t s);
-hipError_t launch_mfma_peak(float* out, int n_workgroups, int iters, hipStream_t stream);
-hipError_t launch_lds_read(float* out, int n_workgroups, int iters, hipStream_t stream);
 int fwd_q_block(int d);
 
 }  // namespace fa

@@ -140,17 +140,20 @@ def test_single_hip_runtime_mapped():
     assert len(_ffi.hip_runtimes_mapped()) <= 1
 
 
-def test_probe_rejects_bad_arguments(lib):
-    assert lib.fa_probe_mfma_peak(None, 4, 4, None) == 1  # FA_ERR_NULL
-    assert lib.fa_probe_mfma_peak(P, 0, 4, None) == 4  # FA_ERR_PARAM
-    assert lib.fa_probe_mfma_peak(P, 4, 0, None) == 4
-    assert lib.fa_probe_mfma_peak(P, (1 << 20) + 1, 4, None) == 4
-    assert lib.fa_probe_mfma_peak(ctypes.c_void_p(0x7F0000000002), 4, 4, None) == 5  # FA_ERR_ALIGN
-    assert lib.fa_probe_lds_read(None, 4, 4, None) == 1
-    assert lib.fa_probe_lds_read(P, 0, 4, None) == 4
-    assert lib.fa_probe_lds_read(P, 4, 0, None) == 4
-    assert lib.fa_probe_lds_read(P, (1 << 20) + 1, 4, None) == 4
-    assert lib.fa_probe_lds_read(ctypes.c_void_p(0x7F0000000002), 4, 4, None) == 5
+def test_fwd_diag_validates_and_matches_elem(lib, ffi):
+    def call(mshift=P, elem=0, q=P, flags=0):
+        return lib.fa_fwd_diag(q, P, P, P, P, None, None, None, None, mshift, 1, 2, 128, 128, 64, 0,
+                               0.125, 1.25, 1, flags, elem, None)
+    assert call(elem=2) == ffi.FA_ERR_PARAM
+    assert call(flags=2) == ffi.FA_ERR_PARAM
+    assert call(q=None) == ffi.FA_ERR_NULL
+    assert call(mshift=ctypes.c_void_p(0x7F0000000002)) == ffi.FA_ERR_ALIGN
+    # shapes and scalars are checked before pointers, as for fa_fwd_elem
+    assert lib.fa_fwd_diag(None, P, P, P, P, None, None, None, None, None, 1, 2, 128, 128, 80, 0,
+                           0.125, 1.25, 1, 0, 0, None) == ffi.FA_ERR_HEADDIM
+    # an empty problem is a no-op whatever the pointers
+    assert lib.fa_fwd_diag(None, None, None, None, None, None, None, None, None, None, 0, 2, 128, 128,
+                           64, 0, 0.125, 1.25, 1, 0, 0, None) == ffi.FA_OK
 
 
 def test_fwd_stats_rejects_bad_arguments(lib):

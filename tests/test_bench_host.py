@@ -33,3 +33,31 @@ def test_recorded_traffic_follows_the_source_digest(tmp_path, monkeypatch):
     assert bench.recorded_traffic("dkdv") == 800.0e6
     assert bench.recorded_traffic("dq") is None  # recorded for other sources: not reported
     assert bench.recorded_traffic("fwd") is None
+
+
+def test_cpu_baseline_reports_parity_of_given_outputs():
+    """The cpu_baseline leg times the oracle and, on the heads it computes, sets the timed step's
+    outputs against it: exact oracle values pass, a perturbed O fails the bar."""
+    import numpy as np
+    import torch
+    import oracle
+    from inputs import CONFIGS, make_inputs
+    cfg = CONFIGS[1]
+    t = make_inputs(cfg)
+    x = {k: v[0, 0].to(torch.float64).numpy() for k, v in t.items()}
+    fr = oracle.forward(x["q"], x["k"], x["v"], cfg.causal, cfg.scale, 1.25, 1)
+    br = oracle.backward(x["q"], x["k"], x["v"], x["do"], cfg.causal, cfg.scale, o=fr.o, lse=fr.lse)
+    gpu = {"o": fr.o[None, None], "lse": fr.lse[None, None], "dq": br.dq[None, None],
+           "dk": br.dk[None, None], "dv": br.dv[None, None], "dup": fr.rs[None, None],
+           "m": fr.m[None, None]}
+    res = bench.cpu_baseline(cfg, t, 1, gpu, budget_s=0.0)
+    par = res["parity_of_timed_step"]
+    assert par["pass"] and par["heads_checked"] == 1 and par["dupcnt_rows_differing"] == 0
+    assert par["shift_m_max_rel_err_where_counts_agree"] == 0.0
+    assert res["host_cpu_count"] == os.cpu_count() and res["kind"] == "oracle"
+    bad = dict(gpu, o=gpu["o"] + 0.05)
+    assert not bench.cpu_baseline(cfg, t, 1, bad, budget_s=0.0)["parity_of_timed_step"]["pass"]
+    bad = dict(gpu, dup=gpu["dup"] + 1)
+    assert bench.cpu_baseline(cfg, t, 1, bad, budget_s=0.0)["parity_of_timed_step"]["dupcnt_rows_differing"] == 128
+    bad = dict(gpu, dq=gpu["dq"] * 1.1)
+    assert not bench.cpu_baseline(cfg, t, 1, bad, budget_s=0.0)["parity_of_timed_step"]["pass"]

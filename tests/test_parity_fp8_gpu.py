@@ -119,7 +119,9 @@ def test_fp8pv_rounding_error_within_bound(fa):
 
 def test_fp8pv_llama_head_and_backward(fa):
     """Half a LLaMA-7B-shaped head (N = 4096, d = 128, causal, mode 1) through the FP8 forward, then
-    the bf16 backward from its O and LSE, against the oracle backward given the same O."""
+    the bf16 backward from its O and LSE: against the oracle backward given the same O (a unit
+    check of the backward), and against the oracle backward given the oracle's own FP8 replay of
+    O and its own LSE (no kernel output enters that reference)."""
     cfg = CONFIGS[4]
     _say("fp8-llama")
     t = make_inputs(cfg, H=1, N=4096)
@@ -132,6 +134,9 @@ def test_fp8pv_llama_head_and_backward(fa):
                          o=o[0, 0].double().cpu().numpy(), lse=fr.lse)
     for name, got, ref in (("dq", dq, br.dq), ("dk", dk, br.dk), ("dv", dv, br.dv)):
         check_grad(got[0, 0].float().cpu().numpy(), ref, name)
+    br_own = oracle.backward(x["q"], x["k"], x["v"], x["do"], cfg.causal, cfg.scale, o=rep["o"], lse=rep["lse"])
+    for name, got, ref in (("dq", dq, br_own.dq), ("dk", dk, br_own.dk), ("dv", dv, br_own.dv)):
+        check_grad(got[0, 0].float().cpu().numpy(), ref, name + " vs the oracle's replay")
 
 
 def test_fp8pv_monitors_and_compensated_sum(fa):

@@ -165,30 +165,63 @@ def test_config4_llama_heads(fa, mode):
         check_head(res, t, 0, h, cfg.causal, cfg.scale, mode, grads=(mode == 1))
 
 
+_C5 = {}
+
+
+def _config5_inputs():
+    if "t" not in _C5:
+        _C5["t"] = make_inputs(CONFIGS[5])
+    return _C5["t"]
+
+
+@pytest.mark.parametrize("heads", [(0, 31), (8, 23)])
 @pytest.mark.parametrize("mode", [1, 2])
-def test_config5_long_tie_grid(fa, mode):
+def test_config5_long_tie_grid(fa, mode, heads):
+    """Tie-heavy long sequence: O, LSE, repeat counts and exact-1.0 counts on four heads (two per
+    case), gradients on head 0.  Mode 2 leaves no exact 1.0 at any row whose maximum is not 0;
+    at a zero maximum the rule does not shift (m = rm = 0), so P^ = 1 at each of its ties.  Mode 1
+    applies the rule per key block from the running (max, count): a block that raises the running
+    maximum to a value seen only once so far exponentiates that key at exactly 1.0 (as the
+    standard softmax does), and so does the first occurrence of a maximum whose repeat arrives in
+    a later block; the counts equal the oracle's block replay exactly."""
     cfg = CONFIGS[5]
-    _say("config5", mode)
-    t = make_inputs(cfg)
-    res = run_fa(fa, t, cfg.causal, cfg.scale, mode, bwd=(mode == 1))
+    _say("config5", mode, heads)
+    t = _config5_inputs()
+    res = run_fa(fa, t, cfg.causal, cfg.scale, mode, bwd=(mode == 1 and 0 in heads))
     bc = fa.fa_fwd_kv_block(cfg.d, cfg.causal)
-    for h in (0, 31):
+    for h in heads:
         fr = check_head(res, t, 0, h, cfg.causal, cfg.scale, mode, grads=(mode == 1 and h == 0),
                         counts_exact=True, ones_exact=True, bc=bc)
         tie_rows = fr.rs > 1
         assert tie_rows.mean() > 0.01
+        ones = res["ones"][0, h]
+        zero = tie_rows & (fr.rm == 0)
         if mode == 2:
-            away = fr.rm != 0
-            assert np.all(res["ones"][0, h][away] == 0), "exact 1.0 in tie-anticipating mode"
-    # repeat counts on more heads via a scores-only pass
-    for h in (5, 17):
-        x = _np64(t, 0, h)
-        rows = np.arange(cfg.N)
-        for r0 in range(0, cfg.N, 2048):
-            blk = rows[r0:r0 + 2048]
-            s = oracle.scaled_scores(x["q"][blk], x["k"], cfg.scale, oracle.visible(blk, cfg.N, True))
-            _, rs = oracle.row_max_and_repeats(s)
-            assert np.array_equal(res["dup"][0, h, blk], rs)
+            assert np.all(ones[fr.rm != 0] == 0), "exact 1.0 in tie-anticipating mode"
+            assert np.array_equal(ones[zero], fr.rs[zero])
+        print(f"config5 head {h} mode {mode}: {tie_rows.sum()} tie rows, {zero.sum()} with a zero "
+              f"maximum; exact 1.0s: {int(ones[fr.rm != 0].sum())} in rows with a nonzero maximum, "
+              f"{int(ones[zero].sum())} at zero tied maxima")
+
+
+def test_config5_repeat_counts_every_head(fa):
+    """Repeat counts of all 32 heads, bit-exact: the oracle's count over the integer dot products
+    of the grid inputs (2q . 2k, exact), one head at a time."""
+    cfg = CONFIGS[5]
+    _say("config5-counts")
+    t = _config5_inputs()
+    g = _to_dev({k_: t[k_] for k_ in ("q", "k", "v")})
+    _, _, dup, _ = fa.forward(g["q"], g["k"], g["v"], cfg.causal, cfg.scale, BETA, 1, stats=True)
+    dup = dup.cpu().numpy()
+    del g
+    n_tie = 0
+    for h in range(cfg.H):
+        q = t["q"][0, h].to(torch.float64).numpy()
+        k = t["k"][0, h].to(torch.float64).numpy()
+        _, rs = oracle.integer_repeat_counts(2 * q, 2 * k, cfg.causal)
+        assert np.array_equal(dup[0, h], rs), f"dupcnt head {h}: {np.sum(dup[0, h] != rs)} rows differ"
+        n_tie += int((rs > 1).sum())
+    print(f"config5: {n_tie} tie rows over {cfg.H} heads, all counts exact")
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -616,3 +649,11 @@ def test_backward_stage_subsets_agree(fa, d, causal, n):
                              lse=lse[0, h].double().cpu().numpy())
         for key, refg in (("dq", br.dq), ("dk", br.dk), ("dv", br.dv)):
             check_grad(ref[key][0, h], refg, f"{key}[{h}]")
+        # and against the oracle's own forward and backward, which see none of the kernel's outputs
+        fr_own = oracle.forward(x["q"], x["k"], x["v"], causal, scale, BETA, 1)
+        check_o(o[0, h].float().cpu().numpy(), fr_own.o)
+        check_lse(lse[0, h].cpu().numpy(), fr_own.lse)
+        br_own = oracle.backward(x["q"], x["k"], x["v"], x["do"], causal, scale)
+        for name, r in runs.items():
+            for key, refg in (("dq", br_own.dq), ("dk", br_own.dk), ("dv", br_own.dv)):
+                check_grad(r[key][0, h], refg, f"{key}[{h}] ({name}) vs the oracle's own backward")
