@@ -62,7 +62,8 @@ typedef enum {
   FA_ERR_HEADDIM = 3, /* d is not 64 or 128 */
   FA_ERR_PARAM = 4,   /* causal, scale, beta, stable_flag, flags, stages or elem out of range */
   FA_ERR_ALIGN = 5,   /* a pointer is not aligned as stated above */
-  FA_ERR_HIP = 6      /* a HIP call failed; see fa_last_hip_error() */
+  FA_ERR_HIP = 6,     /* a HIP call failed; see fa_last_hip_error() */
+  FA_ERR_SCRATCH = 7  /* fa_bwd_noalloc only: the problem needs more rows than its scratch holds */
 } fa_status;
 
 /* Forward pass: writes o [B,H,N,d] bf16 and lse [B,H,N] fp32.  Same as fa_fwd_ex with
@@ -239,6 +240,23 @@ int fa_fwd_fp8pv(const void* q, const void* k, const void* v, void* o, float* ls
 
 /* Bytes of the fa_fwd_fp8pv workspace: B*H*ceil(Nk/128)*(d*128 + 4) (0 for invalid shapes). */
 size_t fa_fwd_fp8pv_workspace_bytes(int B, int H, int Nk, int d);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): fa_bwd without the delta workspace argument.  delta
+ * lives in scratch memory inside the library, one static array per GPU holding
+ * fa_bwd_noalloc_max_rows() fp32 values (2^21, 8 MiB), allocated with the library's code object
+ * and held until the process ends; this call allocates, frees and synchronises nothing.  Every
+ * call on one GPU shares that GPU's array: calls that overlap on one GPU (several streams, several
+ * threads) race on it and must be serialised by the caller.  The array keeps the last call's
+ * contents; nothing in it needs to start at zero (delta is written for every row before it is
+ * read).  Results equal fa_bwd's bit for bit.  Errors as fa_bwd; B*H*N larger than
+ * fa_bwd_noalloc_max_rows() -> FA_ERR_SCRATCH (nothing launched).  The first call on each device
+ * looks up the array's device address (a HIP call, no allocation). */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dO, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, int causal, float scale, float beta, int stable_flag,
+                   void* stream);
+size_t fa_bwd_noalloc_max_rows(void);
 
 /* Bytes of the delta workspace fa_bwd needs: B*H*N*4 (0 for invalid or empty shapes); for
  * fa_bwd_qk pass N = Nq. */

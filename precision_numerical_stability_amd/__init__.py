@@ -20,7 +20,7 @@ import torch  # loaded first so that its HIP runtime is the one this library bin
 
 from . import _ffi
 from ._ffi import (FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_PARAM, FA_ERR_ALIGN,
-                   FA_ERR_HIP, FA_BWD_DELTA, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL,
+                   FA_ERR_HIP, FA_ERR_SCRATCH, FA_BWD_DELTA, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL,
                    FA_FWD_COMPENSATED_SUM, FA_CAUSAL_NONE, FA_CAUSAL_TOP_LEFT,
                    FA_CAUSAL_BOTTOM_RIGHT, FA_ELEM_BF16, FA_ELEM_F16)
 
@@ -39,7 +39,8 @@ __all__ = [
     "fa_fwd", "fa_fwd_ex", "fa_fwd_stats", "fa_fwd_qk", "fa_fwd_elem", "FA_FWD_COMPENSATED_SUM",
     "fa_bwd", "fa_bwd_ex", "fa_bwd_qk", "fa_bwd_elem", "FA_ELEM_BF16", "FA_ELEM_F16",
     "fa_fwd_fp8pv", "fa_fwd_fp8pv_workspace_bytes", "forward_fp8pv",
-    "fa_bwd_workspace_bytes", "fa_fwd_kv_block", "fa_fwd_diag",
+    "fa_bwd_workspace_bytes", "fa_fwd_kv_block", "fa_fwd_diag", "fa_bwd_noalloc",
+    "fa_bwd_noalloc_max_rows",
     "FA_CAUSAL_NONE", "FA_CAUSAL_TOP_LEFT", "FA_CAUSAL_BOTTOM_RIGHT", "fa_status_str",
     "fa_last_hip_error", "FaError", "forward", "backward", "attention", "STANDARD", "TIE_RULE",
     "TIE_ANTICIPATE", "DEFAULT_BETA", "library_path",
@@ -305,6 +306,25 @@ def fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta_ws, causal, scale, beta=DEFAUL
     st = _lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk),
                      _ptr(dv), _ptr(delta_ws), B, H, N, d, int(causal), float(scale), float(beta),
                      int(stable_flag), _stream_handle(q.device, stream))
+    _raise(st)
+
+
+def fa_bwd_noalloc_max_rows() -> int:
+    return int(_lib.fa_bwd_noalloc_max_rows())
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, causal, scale, beta=DEFAULT_BETA,
+                   stable_flag=STANDARD, stream=None):
+    """Call fa_bwd_noalloc on torch tensors (shapes as fa_bwd, no delta workspace): the backward
+    for callers that cannot allocate; delta lives in the library's per-GPU scratch."""
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dO", dO), ("dq", dq), ("dk", dk),
+                    ("dv", dv)):
+        _check(t, name, torch.bfloat16, (B, H, N, d))
+    _check(lse, "lse", torch.float32, (B, H, N))
+    st = _lib.fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq),
+                             _ptr(dk), _ptr(dv), B, H, N, d, int(causal), float(scale), float(beta),
+                             int(stable_flag), _stream_handle(q.device, stream))
     _raise(st)
 
 

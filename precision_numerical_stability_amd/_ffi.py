@@ -16,6 +16,7 @@ FA_ERR_HEADDIM = 3
 FA_ERR_PARAM = 4
 FA_ERR_ALIGN = 5
 FA_ERR_HIP = 6
+FA_ERR_SCRATCH = 7
 
 FA_FWD_COMPENSATED_SUM = 1
 
@@ -47,6 +48,8 @@ SIGNATURES = {
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _I, _P]),
     "fa_bwd_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _I, _I, _P]),
     "fa_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "fa_bwd_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _I, _P]),
+    "fa_bwd_noalloc_max_rows": (ctypes.c_size_t, []),
     "fa_fwd_fp8pv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _I, _I, _P]),
     "fa_fwd_fp8pv_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "fa_fwd_kv_block": (_I, [_I, _I]),

@@ -7,6 +7,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
@@ -102,6 +103,34 @@ int fwd_body(const void* q, const void* k, const void* v, void* o, float* lse, i
   }
   return hip_status(elem == FA_ELEM_F16 ? fa::launch_fwd<fa::kElemF16>(a, d, causal != 0, stable_flag, stats, kahan, s)
                                         : fa::launch_fwd<fa::kElemBf16>(a, d, causal != 0, stable_flag, stats, kahan, s));
+}
+
+// Scratch of the no-allocation backward (fa_bwd_noalloc): delta for up to kScratchRows rows,
+// one copy per GPU the library runs on, held until the process ends.  Host code never uses the
+// array's name as an address (on the host it is only a stand-in for the symbol); the device
+// address comes from hipGetSymbolAddress, looked up once per device with that device current.
+constexpr int64_t kScratchRows = int64_t(1) << 21;  // 8 MiB of fp32
+static __device__ __align__(256) float scratch[kScratchRows];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+float* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of the current device's scratch, or the HIP error of the lookup.
+hipError_t scratch_for_current_device(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = static_cast<float*>(ptr);
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -253,6 +282,28 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
                    stable_flag, FA_BWD_ALL, stream);
 }
 
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal,
+                   float scale, float beta, int stable_flag, void* stream) {
+  // fa_bwd's checks (less the workspace), then the size, all before any HIP call.
+  if (causal != 0 && causal != 1) return FA_ERR_PARAM;
+  const int st = check_common(B, H, N, N, d, causal, scale, beta, stable_flag);
+  if (st != FA_OK) return st;
+  const int64_t rows = int64_t(B) * H * N;
+  if (rows == 0) return FA_OK;
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dO, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
+    return FA_ERR_ALIGN;
+  if (rows > kScratchRows) return FA_ERR_SCRATCH;
+  float* ws = nullptr;
+  const int rc = hip_status(scratch_for_current_device(&ws));
+  if (rc != FA_OK) return rc;
+  return fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, ws, B, H, N, d, causal, scale, beta, stable_flag, stream);
+}
+
+size_t fa_bwd_noalloc_max_rows(void) { return size_t(kScratchRows); }
+
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (B < 0 || H < 0 || N < 0 || (d != 64 && d != 128)) return 0;
   return size_t(B) * size_t(H) * size_t(N) * sizeof(float);
@@ -269,6 +320,7 @@ const char* fa_status_str(int status) {
     case FA_ERR_PARAM: return "FA_ERR_PARAM: causal, scale, beta, stable_flag, flags, stages or elem out of range";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensor pointers must be 16-byte aligned, vectors 4-byte";
     case FA_ERR_HIP: return "FA_ERR_HIP: a HIP call failed (see fa_last_hip_error)";
+    case FA_ERR_SCRATCH: return "FA_ERR_SCRATCH: B*H*N exceeds the rows the no-allocation backward holds (fa_bwd_noalloc_max_rows)";
     default: return "unknown fa_status";
   }
 }

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib, ffi):
 
 
 def test_status_strings(lib):
-    for st in range(7):
+    for st in range(8):
         s = lib.fa_status_str(st).decode()
         assert s.startswith("FA_")
     assert "unknown" in lib.fa_status_str(99).decode()
@@ -138,6 +138,28 @@ def test_single_hip_runtime_mapped():
     import precision_numerical_stability_amd  # noqa: F401
     from precision_numerical_stability_amd import _ffi
     assert len(_ffi.hip_runtimes_mapped()) <= 1
+
+
+def test_bwd_noalloc_validates_before_any_hip_call(lib, ffi):
+    def call(B=1, H=2, N=128, d=64, causal=0, ptrs=None, scale=0.125):
+        p = list(ptrs or [P] * 9)
+        return lib.fa_bwd_noalloc(*p, B, H, N, d, causal, scale, 1.25, 0, None)
+    assert lib.fa_bwd_noalloc_max_rows() == 1 << 21
+    assert call(d=80) == ffi.FA_ERR_HEADDIM
+    assert call(causal=2) == ffi.FA_ERR_PARAM
+    assert call(scale=0.0) == ffi.FA_ERR_PARAM
+    assert call(N=-1) == ffi.FA_ERR_SHAPE
+    assert call(ptrs=[P] * 8 + [None]) == ffi.FA_ERR_NULL
+    assert call(ptrs=[MIS] + [P] * 8) == ffi.FA_ERR_ALIGN
+    assert call(B=0) == ffi.FA_OK  # empty: no-op
+    # one row beyond the scratch: rejected before any launch (fake pointers stay untouched)
+    assert call(B=1, H=1, N=(1 << 21) + 1) == ffi.FA_ERR_SCRATCH
+    assert "FA_ERR_SCRATCH" in lib.fa_status_str(ffi.FA_ERR_SCRATCH).decode()
+
+
+@pytest.mark.skipif(_gpu_present(), reason="needs a host without a GPU (fake pointers would be launched)")
+def test_bwd_noalloc_without_a_device_reports_hip_error(lib, ffi):
+    assert lib.fa_bwd_noalloc(*([P] * 9), 1, 2, 128, 64, 0, 0.125, 1.25, 0, None) == ffi.FA_ERR_HIP
 
 
 def test_fwd_diag_validates_and_matches_elem(lib, ffi):
