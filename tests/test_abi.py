@@ -10,16 +10,27 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa_stable.h")
 
 
-@pytest.fixture(scope="module")
-def lib():
-    from precision_numerical_stability_amd import _ffi
-    return _ffi.load_library()
+def _load_ffi():
+    """The ctypes declarations, loaded by path so that the package (which imports torch and loads
+    the built library) is not imported by the ABI cases themselves."""
+    import importlib.util
+    path = os.path.join(ROOT, "precision_numerical_stability_amd", "_ffi.py")
+    spec = importlib.util.spec_from_file_location("_fa_ffi_abi_test", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
 
 
 @pytest.fixture(scope="module")
 def ffi():
-    from precision_numerical_stability_amd import _ffi
-    return _ffi
+    return _load_ffi()
+
+
+@pytest.fixture(scope="module")
+def lib(ffi):
+    # FA_ABI_TEST_LIBRARY selects another build of the same library (the sanitizer test runs
+    # these cases against a host build instrumented with AddressSanitizer and UBSan).
+    return ffi.load_library(os.environ.get("FA_ABI_TEST_LIBRARY", ffi.LIB_PATH))
 
 
 def _declared_functions():
