@@ -20,7 +20,7 @@
 // instructions, but two waves on one SIMD overlap almost completely when one issues MFMAs and the
 // other vector work.  The 8 waves form two groups (waves 0-3 and 4-7, one of each per SIMD) that
 // run in alternate phases separated by workgroup barriers:
-//   matrix phase M(j): O += V^T P^T of block j-1, then S^T of block j     (MFMA)
+//   matrix phase M(j): S^T of block j, then O += V^T P^T of block j-1     (MFMA)
 //   vector phase V(j): mask, max/count/shift, P^ of block j, rescale O    (VALU)
 // Group A runs M(0) V(0) M(1) V(1) ...; group B runs one phase behind, so in every phase one group
 // works on the matrix cores while the other works on the vector ALUs.  K and V blocks (128 keys
@@ -279,10 +279,12 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   using cpv = std::integral_constant<int, NPV>;
   using cend = std::integral_constant<int, NPV + NSS>;
 
-  // Matrix phase M(j): O = diag(alpha) O + V^T P^T for block j-1 (alpha and P^ from vector phase
-  // j-1), then S^T of block j, at raised wave priority so the matrix cores are fed first when
-  // both waves of a SIMD have work ready.  PAR = j & 1 is a compile-time constant at each call
-  // site, so the LDS buffer addresses fold into instruction offsets.
+  // Matrix phase M(j): S^T of block j, then O = diag(alpha) O + V^T P^T for block j-1 (alpha and
+  // P^ from vector phase j-1), at raised wave priority so the matrix cores are fed first when
+  // both waves of a SIMD have work ready.  The two products are independent; taking S^T first
+  // lets P^ and S^T share registers less (the compiler then needs no scratch in the mode-1
+  // instance).  PAR = j & 1 is a compile-time constant at each call site, so the LDS buffer
+  // addresses fold into instruction offsets.
   auto matrix_phase = [&](int j, auto par_tag) __attribute__((always_inline)) {
     constexpr int PAR = decltype(par_tag)::value;
     const uint16_t* tV = sV[PAR ^ 1];
@@ -296,8 +298,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
       mhh = mlane >> 5;
     }
     __builtin_amdgcn_s_setprio(1);
-    if (pv) m_stream(c0{}, cpv{}, tV, tK);
     if (sc) m_stream(cpv{}, cend{}, tV, tK);
+    if (pv) m_stream(c0{}, cpv{}, tV, tK);
     __builtin_amdgcn_s_setprio(0);
   };
 

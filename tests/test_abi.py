@@ -29,8 +29,14 @@ def ffi():
 @pytest.fixture(scope="module")
 def lib(ffi):
     # FA_ABI_TEST_LIBRARY selects another build of the same library (the sanitizer test runs
-    # these cases against a host build instrumented with AddressSanitizer and UBSan).
-    return ffi.load_library(os.environ.get("FA_ABI_TEST_LIBRARY", ffi.LIB_PATH))
+    # these cases against a host build instrumented with AddressSanitizer and UBSan, without torch).
+    path = os.environ.get("FA_ABI_TEST_LIBRARY")
+    if path is None:
+        # As in the package: torch first, so that the library binds to torch's HIP runtime and the
+        # binding tests below, which import torch, still see one runtime in this process.
+        import torch  # noqa: F401
+        path = ffi.LIB_PATH
+    return ffi.load_library(path)
 
 
 def _declared_functions():
