@@ -275,6 +275,12 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
 // A block is processed as four 32-query sub-blocks in one straight-line software pipeline: the
 // S/dP products of sub-block t+1 are issued before the softmax-gradient arithmetic of sub-block t,
 // so the matrix cores work on the next sub-block while the vector ALUs finish the current one.
+//
+// Registers: dK and dV accumulate in AGPRs (builtin MFMAs), S and dP are produced in VGPRs
+// (VGPR-form MFMAs, mfma32x32x16_vgpr) so the gradient arithmetic reads them with no copy out of
+// the accumulation registers, and the K/V fragments, used only as the B operand of those MFMAs,
+// sit in AGPRs.  The gradient arithmetic reads S/dP of a sub-block whose products were issued at
+// least one 16-step phase earlier, well past the MFMA's result hazard.
 constexpr int kDkvBq = 128;
 constexpr int kDkvBk = 128;
 
@@ -385,9 +391,9 @@ __device__ __forceinline__ void dkdv_block(const uint16_t* tQ, const uint16_t* t
     if constexpr (S::is_sdp(k)) {
       constexpr int ks = i >> 1;
       if constexpr ((i & 1) == 0) {
-        s[c] = mfma32x32x16<E>(op, f.k[ks], ks == 0 ? zero16() : s[c]);
+        s[c] = mfma32x32x16_vgpr<E, ks == 0>(op, f.k[ks], s[c]);
       } else {
-        dp[c] = mfma32x32x16<E>(op, f.v[ks], ks == 0 ? zero16() : dp[c]);
+        dp[c] = mfma32x32x16_vgpr<E, ks == 0>(op, f.v[ks], dp[c]);
       }
     } else {
       constexpr int half = i / (2 * DT), dt = (i >> 1) % DT, o4 = 4 * half;

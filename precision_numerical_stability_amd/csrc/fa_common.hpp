@@ -66,6 +66,28 @@ __device__ __forceinline__ f32x16 mfma32x32x16(e16x8 a, e16x8 b, f32x16 c) {
   }
 }
 
+// v_mfma_f32_32x32x16_{bf16,f16} in the VGPR form with the B operand read from AGPRs: the result
+// (and the accumulator it continues) lives in VGPRs, where vector instructions can read it
+// directly, while a loop-invariant B operand occupies accumulation registers instead.  The
+// compiler's builtin picks one form for every MFMA of a kernel (the AGPR form, once a kernel needs
+// more than 256 registers), so a kernel that wants both forms issues this one as inline assembly.
+// ZERO: the accumulator input is the constant 0; the destination is then early-clobber, since a
+// multi-pass MFMA must not write registers it is still reading A or B from.  The compiler still
+// tracks the asm operands for waits on loads and for wait states after the MFMA; a vector read of
+// the result must come later in the instruction stream than the hazard distance of a 32x32 MFMA.
+template <int E, bool ZERO>
+__device__ __forceinline__ f32x16 mfma32x32x16_vgpr(e16x8 a, e16x8 b_acc, f32x16 c) {
+  f32x16 d;
+  if constexpr (E == kElemF16) {
+    if constexpr (ZERO) asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b_acc));
+    else asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "a"(b_acc), "0"(c));
+  } else {
+    if constexpr (ZERO) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b_acc));
+    else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "a"(b_acc), "0"(c));
+  }
+  return d;
+}
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
