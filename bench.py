@@ -41,8 +41,10 @@ def parse():
     ap.add_argument("--config", type=int, default=4, help="workload id (1-5)")
     ap.add_argument("--mode", type=int, default=1, help="stable_flag: 0, 1 or 2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-fp8pv", action="store_true",
-                    help="skip the FP8 P^V forward leg (fa_fwd_fp8pv on the same bf16 inputs)")
+    ap.add_argument("--fp8pv", action="store_true",
+                    help="also time the FP8 P^V forward (fa_fwd_fp8pv on the same bf16 inputs); off by "
+                         "default: with its V pre-pass it runs a few percent slower than the bf16 forward")
+    ap.add_argument("--no-fp8pv", action="store_true", help=argparse.SUPPRESS)  # the default now
     ap.add_argument("--no-f16", action="store_true",
                     help="skip the fp16 leg (the same workload with fp16 inputs, reported beside "
                          "the bf16 headline)")
@@ -268,7 +270,7 @@ def main():
     # FP8 P^V leg: the forward with its P^ V product in E4M3 (V quantised per 128-key block by the
     # library's pre-pass, which runs inside the timed call), on the same bf16 inputs.
     fp8pv = None
-    if not args.no_fp8pv:
+    if args.fp8pv and not args.no_fp8pv:
         ws8 = torch.empty(fa.fa_fwd_fp8pv_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
         o8 = torch.empty_like(q)
 
