@@ -334,11 +334,13 @@ struct DkvSched {
     if (p % 2 == 1) return 8 * p + ((L == 16) ? j / 2 : j);
     return 8 * p + ((L == 16) ? (j - 1) / 2 : j);
   }
-  // Halves whose LSE/delta vectors are read from LDS at step k (four steps before the phase that
-  // uses them): returns a bit mask over g.
+  // Halves whose LSE/delta vectors are read from LDS at step k: returns a bit mask over g.  Half
+  // g + 1 is read at the start of phase g, a whole phase ahead of its use (its register slot's
+  // previous half, g - 1, finished in phase g - 1), except in phase 1, which runs halves 0 and 1:
+  // there half 2 is read once half 0, which still uses that slot, is done (step L / 2).
   static constexpr int ld_halves(int k) {
     const int p = phase(k), j = k % L;
-    if (j != L - 4 || p + 1 >= 2 * SB) return 0;
+    if (j != (p == 1 ? L / 2 : 0) || p + 1 >= 2 * SB) return 0;
     return (p == 0) ? 0x3 : (1 << (p + 1));
   }
 };
