@@ -441,8 +441,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
     } else {
       rs.lsum = alpha * rs.lsum + psum;
     }
-    // O is rescaled by alpha at the start of the next matrix phase, before this block is added
-    // (alpha == 1 exactly changes nothing, so a wave where no lane's shift moved skips it).
+    // O is rescaled by alpha in the next matrix phase, before this block is added.  The rescale
+    // runs in every matrix phase: skipping it for a wave whose alphas are all 1 needs a second
+    // copy of the P^V stream behind a branch, and with it the register allocator spills.
     alpha_pending = oscale;
   };
 
