@@ -250,8 +250,10 @@ size_t fa_fwd_fp8pv_workspace_bytes(int B, int H, int Nk, int d);
  * threads) race on it and must be serialised by the caller.  The array keeps the last call's
  * contents; nothing in it needs to start at zero (delta is written for every row before it is
  * read).  Results equal fa_bwd's bit for bit.  Errors as fa_bwd; B*H*N larger than
- * fa_bwd_noalloc_max_rows() -> FA_ERR_SCRATCH (nothing launched).  The first call on each device
- * looks up the array's device address (a HIP call, no allocation). */
+ * fa_bwd_noalloc_max_rows() -> FA_ERR_SCRATCH (nothing launched).  The array used is that of the
+ * GPU the stream belongs to (the current device for the default stream); the first call for each
+ * GPU looks up its address (HIP calls, no allocation), with that GPU made current for the lookup
+ * and the caller's current device restored. */
 int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
                    const void* dO, void* dq, void* dk, void* dv,
                    int B, int H, int N, int d, int causal, float scale, float beta, int stable_flag,

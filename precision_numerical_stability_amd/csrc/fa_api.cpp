@@ -117,15 +117,34 @@ std::once_flag g_scratch_once[kMaxDevices];
 float* g_scratch_ptr[kMaxDevices];
 hipError_t g_scratch_err[kMaxDevices];
 
-// Device address of the current device's scratch, or the HIP error of the lookup.
-hipError_t scratch_for_current_device(float** out) {
+// Device address of the scratch on the GPU that `stream` runs on (the current device for the
+// default stream), or the HIP error of the lookup.  The kernels go to that stream, so they must
+// get that GPU's copy of the array; its first lookup makes the GPU current for the call and
+// restores the caller's device afterwards.
+hipError_t scratch_for_stream(hipStream_t stream, float** out) {
   int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
+  hipError_t e;
+  if (stream != nullptr) {
+    hipDevice_t d = -1;
+    e = hipStreamGetDevice(stream, &d);
+    dev = static_cast<int>(d);
+  } else {
+    e = hipGetDevice(&dev);
+  }
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   std::call_once(g_scratch_once[dev], [dev]() {
+    int cur = -1;
+    hipError_t r = hipGetDevice(&cur);
+    const bool switch_dev = (r == hipSuccess && cur != dev);
+    if (switch_dev) r = hipSetDevice(dev);
     void* ptr = nullptr;
-    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (r == hipSuccess) r = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (switch_dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (r == hipSuccess) r = back;
+    }
+    g_scratch_err[dev] = r;
     g_scratch_ptr[dev] = static_cast<float*>(ptr);
   });
   if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
@@ -297,7 +316,7 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, c
     return FA_ERR_ALIGN;
   if (rows > kScratchRows) return FA_ERR_SCRATCH;
   float* ws = nullptr;
-  const int rc = hip_status(scratch_for_current_device(&ws));
+  const int rc = hip_status(scratch_for_stream(static_cast<hipStream_t>(stream), &ws));
   if (rc != FA_OK) return rc;
   return fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, ws, B, H, N, d, causal, scale, beta, stable_flag, stream);
 }

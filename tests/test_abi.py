@@ -1,5 +1,9 @@
 """C ABI checks that need no GPU: the library loads, exports what include/fa_stable.h declares,
-and rejects bad arguments before any HIP call (fake pointers are never dereferenced)."""
+and rejects bad arguments before any HIP call (fake pointers are never dereferenced).
+
+A call whose arguments are all valid gets as far as a kernel launch; with the fake pointers used
+here that launch may only happen on a host without a GPU (where it fails with a HIP error), so
+every such case sits in a test skipped where a GPU is present."""
 import ctypes
 import os
 import re
@@ -299,9 +303,15 @@ def test_fp8pv_entry_point_validates(lib, ffi):
     assert call(q=None) == ffi.FA_ERR_NULL
     assert call(d=96) == ffi.FA_ERR_HEADDIM and call(flag=3) == ffi.FA_ERR_PARAM
     assert call(causal=3) == ffi.FA_ERR_PARAM and call(flags=2) == ffi.FA_ERR_PARAM
-    assert call(ws=None, Nk=0) != ffi.FA_ERR_NULL  # no keys: no workspace needed
     assert call(B=0, q=None, ws=None) == ffi.FA_OK
     assert lib.fa_fwd_fp8pv_workspace_bytes(1, 2, 300, 64) == 2 * 3 * (64 * 128 + 4)
     assert lib.fa_fwd_fp8pv_workspace_bytes(1, 32, 8192, 128) == 32 * 64 * (128 * 128 + 4)
     assert lib.fa_fwd_fp8pv_workspace_bytes(1, 1, 0, 128) == 0
     assert lib.fa_fwd_fp8pv_workspace_bytes(1, 1, 8, 80) == 0
+
+
+@pytest.mark.skipif(_gpu_present(), reason="needs a host without a GPU (fake pointers would be launched)")
+def test_fp8pv_without_keys_needs_no_workspace_without_a_device(lib, ffi):
+    # No keys: the NULL workspace is accepted and the call goes on to launch (which fails here).
+    assert lib.fa_fwd_fp8pv(P, P, P, P, P, None, None, None, None, None, 1, 2, 128, 0, 64, 1, 0.125,
+                            1.25, 1, 0, None) == ffi.FA_ERR_HIP

@@ -1,6 +1,7 @@
 """The no-allocation backward (fa_bwd_noalloc, through the C ABI) against fa_bwd with a caller
-workspace: two calls in a row, the second on a smaller problem, each bit-identical to fa_bwd and
-within the gradient bar of the oracle on one head; a problem beyond the scratch is refused."""
+workspace: calls in a row, the second on a smaller problem, the third on a stream the test creates
+(the scratch is looked up through the stream's device), each bit-identical to fa_bwd and within
+the gradient bar of the oracle on one head; a problem beyond the scratch is refused."""
 import ctypes
 
 import numpy as np
@@ -31,10 +32,13 @@ def _p(t):
 def test_no_alloc_backward_matches_workspace_backward(fa):
     from precision_numerical_stability_amd import _ffi
     lib = _ffi.load_library()
-    stream = torch.cuda.current_stream()
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream(device=DEV)  # default priority
     # the second problem is smaller: the scratch keeps the first call's delta beyond its rows
-    for (B, H, N, d, causal, seed) in ((2, 4, 1000, 128, True, 3100), (1, 3, 333, 64, False, 3101)):
-        print(f"[case] noalloc B={B} H={H} N={N} d={d} causal={causal}", flush=True)
+    cases = ((2, 4, 1000, 128, True, 3100, False), (1, 3, 333, 64, False, 3101, False),
+             (1, 2, 700, 128, True, 3102, True))
+    for (B, H, N, d, causal, seed, on_side) in cases:
+        print(f"[case] noalloc B={B} H={H} N={N} d={d} causal={causal} side_stream={on_side}", flush=True)
         t = randn_inputs(B, H, N, d, seed=seed)
         g = {k: v.to(DEV) for k, v in t.items()}
         scale = d ** -0.5
@@ -43,6 +47,9 @@ def test_no_alloc_backward_matches_workspace_backward(fa):
         delta = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
         fa.fa_bwd(g["q"], g["k"], g["v"], o, lse, g["do"], *ref, delta, causal, scale)
         got = [torch.full_like(g["q"], 7.0) for _ in range(3)]
+        stream = side if on_side else main
+        if on_side:
+            side.wait_stream(main)  # the inputs and outputs were written on the main stream
         rc = lib.fa_bwd_noalloc(_p(g["q"]), _p(g["k"]), _p(g["v"]), _p(o), _p(lse), _p(g["do"]),
                                 *(_p(x) for x in got), B, H, N, d, int(causal), scale, 1.25, 1,
                                 ctypes.c_void_p(stream.cuda_stream))
