@@ -251,19 +251,11 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
     if (j < n_kv) step(masked{}, buf1{});
   }
 
-  if (qrow < Nq) {
-    uint16_t* dst = a.dq + qoff + (int64_t)qrow * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int d0 = 32 * dt + 8 * rr + 4 * hh;
-        i32x2 w;
-        w[0] = (int)pack2<E>(acc[dt][4 * rr] * a.scale, acc[dt][4 * rr + 1] * a.scale);
-        w[1] = (int)pack2<E>(acc[dt][4 * rr + 2] * a.scale, acc[dt][4 * rr + 3] * a.scale);
-        *reinterpret_cast<i32x2*>(dst + d0) = w;
-      }
-  }
+  // dQ rows of this wave's 32 queries, through the K buffers (the last step ended with a barrier
+  // and issued no loads).
+  const int qw0 = q0 + wave * 32;
+  store_rows_via_lds<E, D>(reinterpret_cast<uint8_t*>(&sK[0][0]) + wave * (64 * D), a.dq + qoff + (int64_t)qw0 * D,
+                           Nq - qw0, lane, [&](int dt, int r) { return acc[dt][r] * a.scale; });
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -581,23 +573,13 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   if (i < n_full) step(plain{}, buf0{});
   if (i < n_q) step(masked{}, buf);
 
-  if (key < Nk) {
-    uint16_t* dkr = a.dk + koff + (int64_t)key * D;
-    uint16_t* dvr = a.dv + koff + (int64_t)key * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int d0 = 32 * dt + 8 * rr + 4 * hh;
-        i32x2 wk, wv;
-        wk[0] = (int)pack2<E>(dk[dt][4 * rr] * a.scale, dk[dt][4 * rr + 1] * a.scale);
-        wk[1] = (int)pack2<E>(dk[dt][4 * rr + 2] * a.scale, dk[dt][4 * rr + 3] * a.scale);
-        wv[0] = (int)pack2<E>(dv[dt][4 * rr], dv[dt][4 * rr + 1]);
-        wv[1] = (int)pack2<E>(dv[dt][4 * rr + 2], dv[dt][4 * rr + 3]);
-        *reinterpret_cast<i32x2*>(dkr + d0) = wk;
-        *reinterpret_cast<i32x2*>(dvr + d0) = wv;
-      }
-  }
+  // dK and dV rows of this wave's 32 keys, through the Q and dO buffers (no wave reads them any
+  // more: the last step ended with a barrier and issued no loads).
+  const int rows_left = Nk - kw0;
+  store_rows_via_lds<E, D>(reinterpret_cast<uint8_t*>(&sQ[0][0]) + wave * (64 * D), a.dk + koff + (int64_t)kw0 * D,
+                           rows_left, lane, [&](int dt, int r) { return dk[dt][r] * a.scale; });
+  store_rows_via_lds<E, D>(reinterpret_cast<uint8_t*>(&sG[0][0]) + wave * (64 * D), a.dv + koff + (int64_t)kw0 * D,
+                           rows_left, lane, [&](int dt, int r) { return dv[dt][r]; });
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -305,6 +305,40 @@ struct DirectStage {
   }
 };
 
+// Store a wave's 32 output rows of D 16-bit elements held as the transposed accumulator tiles of
+// 32x32 products (tile dt, register r of lane l: row l % 32, column 32 dt + 8 (r / 4) + 4 (l / 32)
+// + r % 4).  Stored directly, every store instruction would put 8 bytes into each of 32 rows,
+// 32 cache lines per instruction, and the vector memory pipeline takes about a line per cycle.
+// Instead the rows go through LDS: each lane packs its pieces into this wave's stage area (32
+// rows of 2D bytes, 16-byte chunk c of row r at chunk c ^ (r % (2D / 16)), which spreads both
+// access patterns over the banks), then reads back 16-byte chunks in row order and stores them,
+// so that each store instruction writes whole consecutive rows (the 32 rows are consecutive in
+// memory, dst pointing at the first).  A wave reads only what it wrote itself, and one wave's LDS
+// operations complete in order, so no barrier is needed; the caller makes sure no other wave still
+// reads that LDS.  Rows from n_rows on are not stored.  value(dt, r) gives the element.
+template <int E, int D, typename F>
+__device__ __forceinline__ void store_rows_via_lds(uint8_t* stage, uint16_t* dst, int n_rows, int lane, F&& value) {
+  constexpr int RB = 2 * D;     // bytes per row
+  constexpr int CPR = RB / 16;  // 16-byte chunks per row
+  const int l32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      i32x2 w;
+      w[0] = (int)pack2<E>(value(dt, 4 * rr), value(dt, 4 * rr + 1));
+      w[1] = (int)pack2<E>(value(dt, 4 * rr + 2), value(dt, 4 * rr + 3));
+      const int chunk = (4 * dt + rr) ^ (l32 % CPR);
+      *reinterpret_cast<i32x2*>(stage + l32 * RB + 16 * chunk + 8 * hh) = w;
+    }
+#pragma unroll
+  for (int i = 0; i < 32 * CPR / 64; ++i) {
+    const int c = 64 * i + lane, row = c / CPR, col = c % CPR;
+    const i32x4 v = *reinterpret_cast<const i32x4*>(stage + row * RB + 16 * (col ^ (row % CPR)));
+    if (row < n_rows) *reinterpret_cast<i32x4*>(dst + (int64_t)row * D + 8 * col) = v;
+  }
+}
+
 // Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E - 1, so that the body can
 // use the index in constant expressions (register-array indices, if constexpr).
 template <int B, int E, typename F>

@@ -489,27 +489,19 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
   const float ltot = KAHAN ? halves_sum(rs.lsum - rs.lcomp) : halves_sum(rs.lsum);
   const float row_min = STATS ? halves_min(rs.run_min) : 0.f;
   const int ones_tot = STATS ? halves_sum_i(rs.n_ones) : 0;
+  // A query that sees no key (no keys at all, or bottom-right alignment with more queries than
+  // keys) has the empty sum: O = 0 and LSE = -inf.  Its lanes ran with an infinite max, so their
+  // accumulators are not used.
+  const bool empty = (Nk == 0) || (CAUSAL && qrow + a.coff < 0);
+  // FP8: ltot is 2^8 l and O is held in units of vs / 2^8, so O = oacc vs / ltot.
+  const float inv = empty ? 0.f : (FP8 ? rs.vs / ltot : 1.f / ltot);
+  // O rows of this wave's 32 queries, through the tile buffers (waves 0-3 in the K buffers, 4-7 in
+  // the V buffers): both groups have passed the last barrier, so no wave reads them any more, and
+  // the last iterations issued no loads.
+  store_rows_via_lds<E, D>(
+      reinterpret_cast<uint8_t*>(wave < 4 ? &sK[0][0] : &sV[0][0]) + (wave & 3) * (64 * D), a.o + qoff + (int64_t)qw0 * D,
+      Nq - qw0, lane, [&](int dt, int r) { return empty ? 0.f : oacc[dt][r] * inv; });
   if (qrow < Nq) {
-    // A query that sees no key (no keys at all, or bottom-right alignment with more queries than
-    // keys) has the empty sum: O = 0 and LSE = -inf.  Its lanes ran with an infinite max, so their
-    // accumulators are not used.
-    const bool empty = (Nk == 0) || (CAUSAL && qrow + a.coff < 0);
-    // FP8: ltot is 2^8 l and O is held in units of vs / 2^8, so O = oacc vs / ltot.
-    const float inv = empty ? 0.f : (FP8 ? rs.vs / ltot : 1.f / ltot);
-    uint16_t* orow = a.o + qoff + (int64_t)qrow * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int d0 = 32 * dt + 8 * rr + 4 * hh;
-        float x[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) x[u] = empty ? 0.f : oacc[dt][4 * rr + u] * inv;
-        i32x2 w;
-        w[0] = (int)pack2<E>(x[0], x[1]);
-        w[1] = (int)pack2<E>(x[2], x[3]);
-        *reinterpret_cast<i32x2*>(orow + d0) = w;
-      }
     if (hh == 0) {
       const int64_t ri = (int64_t)bh * Nq + qrow;
       a.lse[ri] = empty ? -INFINITY : (rs.m2 + __log2f(ltot) - (FP8 ? 8.f : 0.f)) * kLn2;
