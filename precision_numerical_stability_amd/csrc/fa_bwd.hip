@@ -58,7 +58,8 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// dQ: one workgroup per (128-query tile, head), 4 waves of 32 queries; loops over 64-key blocks.
+// dQ at d = 64 (d = 128 runs dqw_kernel below): one workgroup per (128-query tile, head), 4 waves
+// of 32 queries; loops over 64-key blocks.
 // Lane layout as in the forward: S^T = K Q^T and dP^T = V dO^T put one query per lane, so LSE
 // and delta are lane-local; dQ^T = K^T dS^T takes dS^T from the accumulator registers.  Within a
 // block, the S/dP products of the second 32-key half are issued before the dS arithmetic of the
@@ -256,6 +257,403 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
   const int qw0 = q0 + wave * 32;
   store_rows_via_lds<E, D>(reinterpret_cast<uint8_t*>(&sK[0][0]) + wave * (64 * D), a.dq + qoff + (int64_t)qw0 * D,
                            Nq - qw0, lane, [&](int dt, int r) { return acc[dt][r] * a.scale; });
+}
+
+// ---------------------------------------------------------------------------------------------
+// dQ at d = 128: one workgroup per (256-query tile, head), 4 waves of 64 queries, one wave per
+// SIMD.  A wave's queries form two 32-query halves, and every K or V operand it reads from LDS
+// feeds the MFMAs of both halves: half the LDS operand bytes per MFMA of a 32-query wave.  The Q
+// and dO fragments (B operands of S^T and dP^T, 128 registers) and the dQ^T accumulators (128)
+// fill the accumulation registers; S/dP tiles, packed dS and the operand ring use the others.
+//
+// Keys come in 64-key blocks of two 32-key sub-blocks, staged in three LDS buffers.  The work is
+// one software pipeline over the 32-key sub-blocks u of the key range: unit u issues the S/dP
+// products of u + 1, runs the dS arithmetic of u beside them, and the dQ products of u - 1, so no
+// MFMA waits on vector work finished just before it.  The iteration over key block j runs units
+// 2j - 1 and 2j: its S/dP products read block j, its dQ products block j - 1, while block j + 1
+// loads into the third buffer.  In the first iteration, units -1 and -2 run on neutral data (an
+// infinite LSE makes their dS zero, and the K buffer they read is zeroed); the last block's
+// remaining dS and dQ work drains after the loop.
+//
+// The S^T and dP^T products are VGPR-form inline-asm MFMAs (mfma32x32x16_vgpr), for which the
+// compiler inserts no wait states.  Their results are read at least a few MFMAs later, and their
+// B operands, the Q and dO fragments, are moved to the accumulation registers once, before the
+// first iteration, so that no vector write of an operand lands just before such an MFMA.
+constexpr int kDqwBc = 64;
+constexpr int kDqwBr = 256;
+constexpr int kDqwBuf = 3;
+constexpr int kDqwIssueStep = 3;  // MFMA step of an iteration after which the next block's loads issue
+
+template <int D>
+struct DqwSched {
+  static constexpr int KS = D / 16, DT = D / 32;
+  static constexpr int USTEP = 6 * KS;     // MFMA steps per unit: KS groups of 6
+  static constexpr int NSTEP = 2 * USTEP;  // per iteration
+  static constexpr int NPAIR = NSTEP / 2;  // operand reads per iteration, one per two MFMAs
+  static_assert(KS == 2 * DT, "each group of a unit carries one dQ operand");
+  // Step k of an iteration: unit k / USTEP; within it group g = (k % USTEP) / 6 and slot
+  // w = k % 6, of kind w / 2 (0: dQ^T += K^T dS^T, 1: S^T = K Q^T, 2: dP^T = V dO^T) for query
+  // half w % 2.  The operand of steps 2p and 2p + 1 is read once (pair p).  Element e (0..31) of
+  // a unit's dS arithmetic runs after step pos(uu, e) of that unit; -1 places it before the
+  // unit's first step (in unit 0, beside the operand reads that start the iteration).
+  static constexpr int pos(int uu, int e) { return e * USTEP / 32 - (uu == 0 ? 1 : 0); }
+};
+
+// LDS byte addresses of this lane's operand reads, relative to the first K or V buffer: rows
+// (16-byte reads of row l % 32 at k-slice g) of K and of V, and the two halves of a transposed
+// read of K at d-tile dt.  Every read adds a compile-time buffer and row offset, which folds into
+// the instruction.  Each iteration passes the patterns through an empty asm statement, so the
+// compiler keeps one copy of each instead of hoisting a sum per buffer out of the loop.
+template <int D>
+struct DqwAddr {
+  uint32_t rk[D / 16], rv[D / 16], tk[D / 32][2];
+  __device__ __forceinline__ void init(uint32_t base_k, uint32_t base_v, int lane) {
+    const int l32 = lane & 31, hh = lane >> 5, s = lane & 15;
+#pragma unroll
+    for (int g = 0; g < D / 16; ++g) {
+      const uint32_t off = 2u * (uint32_t)lds_off<D>(l32, 16 * g + 8 * hh);
+      rk[g] = base_k + off;
+      rv[g] = base_v + off;
+    }
+    const int r1 = 4 * hh + (s >> 2);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int col = 32 * dt + (((lane >> 4) & 1) << 4) + ((s & 3) << 2);
+      tk[dt][0] = base_k + 2u * (uint32_t)lds_off<D>(r1, col);
+      tk[dt][1] = base_k + 2u * (uint32_t)lds_off<D>(r1 + 8, col);
+    }
+  }
+  __device__ __forceinline__ void opaque() {
+#pragma unroll
+    for (int g = 0; g < D / 16; ++g) asm volatile("" : "+v"(rk[g]), "+v"(rv[g]));
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) asm volatile("" : "+v"(tk[dt][0]), "+v"(tk[dt][1]));
+  }
+};
+
+__device__ __forceinline__ e16x8 lds_ld128(uint32_t a) {
+  return as_e16x8(*reinterpret_cast<const __attribute__((address_space(3))) i32x4*>((uintptr_t)a));
+}
+// Transposed operand read (see lds_read_col8_tr) from the two half addresses.
+__device__ __forceinline__ e16x8 lds_ld_tr(uint32_t a0, uint32_t a1) {
+  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((uintptr_t)a0));
+  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((uintptr_t)a1));
+  i32x2 x = __builtin_bit_cast(i32x2, lo);
+  i32x2 y = __builtin_bit_cast(i32x2, hi);
+  return make_e16x8((uint32_t)x[0], (uint32_t)x[1], (uint32_t)y[0], (uint32_t)y[1]);
+}
+
+template <int D>
+struct DqwState {
+  f32x16 s[2][2], dp[2][2];  // [set][query half]: S^T and dP^T of sub-block u live in set u & 1
+  uint32_t pds[2][2][8];     // packed dS^T, [set][query half][pair of keys]
+  f32x16 acc[2][D / 32];     // dQ^T, [query half][d-tile]
+  e16x8 qf[2][D / 16], gf[2][D / 16];
+};
+
+// Element arithmetic of one unit's sub-block (set c): P = exp2(S scale log2e - LSE log2e),
+// dS = P (dP - delta), pairs packed to the element type.  Masked: key key0 + cc + 4h (cc = 8 (r / 4)
+// + r % 4, relative to the causal offset) is hidden from the half's query when cc > lim.
+template <int E, int D, bool MASK, int C, int A, int R>
+__device__ __forceinline__ void dqw_elem(DqwState<D>& st, float sl2, float L, float dl, int lim, float& tmp) {
+  float p = fast_exp2(fmaf(st.s[C][A][R], sl2, -L));
+  if (MASK) {
+    constexpr int cc = 8 * (R >> 2) + (R & 3);
+    p = (cc > lim) ? 0.f : p;
+  }
+  const float ds = p * (st.dp[C][A][R] - dl);
+  if constexpr ((R & 1) == 0) tmp = ds;
+  else st.pds[C][A][R >> 1] = pack2<E>(tmp, ds);
+}
+
+template <bool CAUSAL>
+__device__ __forceinline__ int dqw_lim(int qrow, int key0, int nk, int hh) {
+  return min(CAUSAL ? qrow - key0 - 4 * hh : INT_MAX, nk - 1 - key0 - 4 * hh);
+}
+
+// One iteration (key block j; kv0 = 64 j - coff, nk = Nk - coff): the buffer B holds block j,
+// buffer (B + 2) % 3 block j - 1; issue() sends block j + 1's loads to the third buffer.  lse:
+// LSE log2e of the two query halves for unit 2j; lsep the same for unit 2j - 1 (infinite in the
+// first iteration).
+template <int E, int D, bool CAUSAL, bool MASK, int B, typename Issue>
+__device__ __forceinline__ void dqw_iter(DqwAddr<D>& ad, int kv0, int nk, const int (&qrow)[2], int lane, float sl2,
+                                         const float (&lse)[2], const float (&lsep)[2], const float (&dlt)[2],
+                                         DqwState<D>& st, Issue&& issue) {
+  using S = DqwSched<D>;
+  constexpr int DT = D / 32;
+  constexpr int DP = 4;       // pairs read ahead
+  constexpr int RING = DP + 1;
+  constexpr uint32_t TILE = kDqwBc * D * 2;
+  constexpr uint32_t OFF = B * TILE, OFFP = ((B + 2) % kDqwBuf) * TILE;  // block j, block j - 1
+  const int hh = lane >> 5;
+  ad.opaque();
+  e16x8 ring[RING];
+  int lim[2][2] = {{INT_MAX, INT_MAX}, {INT_MAX, INT_MAX}};  // [unit][query half]
+  if (MASK) {
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) lim[uu][h] = dqw_lim<CAUSAL>(qrow[h], kv0 - 32 + 32 * uu, nk, hh);
+  }
+  float tmp = 0.f;
+
+  auto read_pair = [&](auto pc) __attribute__((always_inline)) {
+    constexpr int p = decltype(pc)::value;
+    constexpr int k = 2 * p, uu = k / S::USTEP, kk = k % S::USTEP, g = kk / 6, kind = (kk % 6) / 2;
+    if constexpr (kind == 0) {
+      constexpr int kh = g / DT, dt = g % DT;
+      constexpr uint32_t o = OFFP + (32 * uu + 16 * kh) * 2 * D;
+      ring[p % RING] = lds_ld_tr(ad.tk[dt][0] + o, ad.tk[dt][1] + o);
+    } else {
+      constexpr uint32_t o = OFF + 32 * uu * 2 * D;
+      ring[p % RING] = lds_ld128((kind == 1 ? ad.rk[g] : ad.rv[g]) + o);
+    }
+  };
+  auto mfma_step = [&](auto kc) __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
+    constexpr int uu = k / S::USTEP, kk = k % S::USTEP, g = kk / 6, w = kk % 6, kind = w / 2, h = w % 2;
+    const e16x8 op = ring[(k / 2) % RING];
+    if constexpr (kind == 0) {
+      constexpr int kh = g / DT, dt = g % DT, o = 4 * kh;
+      st.acc[h][dt] = mfma32x32x16<E>(
+          op, make_e16x8(st.pds[uu][h][o], st.pds[uu][h][o + 1], st.pds[uu][h][o + 2], st.pds[uu][h][o + 3]),
+          st.acc[h][dt]);
+    } else if constexpr (kind == 1) {
+      st.s[uu][h] = mfma32x32x16_vgpr<E, g == 0>(op, st.qf[h][g], st.s[uu][h]);
+    } else {
+      st.dp[uu][h] = mfma32x32x16_vgpr<E, g == 0>(op, st.gf[h][g], st.dp[uu][h]);
+    }
+  };
+  // Elements of unit uu at position kk: the sub-block in set 1 - uu.
+  auto elems_at = [&](auto uc, auto kc) __attribute__((always_inline)) {
+    constexpr int uu = decltype(uc)::value, kk = decltype(kc)::value;
+    static_for<0, 32>([&](auto ec) __attribute__((always_inline)) {
+      constexpr int e = decltype(ec)::value;
+      if constexpr (S::pos(uu, e) == kk) {
+        constexpr int h = e / 16, r = e % 16;
+        dqw_elem<E, D, MASK, 1 - uu, h, r>(st, sl2, uu == 0 ? lsep[h] : lse[h], dlt[h], lim[uu][h], tmp);
+      }
+    });
+  };
+
+  __builtin_amdgcn_sched_barrier(0);
+  static_for<0, DP>([&](auto pc) __attribute__((always_inline)) { read_pair(pc); });
+  // The first elements read S/dP of the previous iteration's last MFMAs, issued as inline asm, for
+  // which the compiler inserts no wait states: wait them out here (once per iteration).
+  asm volatile("s_nop 7\n\ts_nop 3");
+  __builtin_amdgcn_sched_barrier(0);
+  elems_at(std::integral_constant<int, 0>{}, std::integral_constant<int, -1>{});
+  static_for<0, S::NSTEP>([&](auto kc) __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
+    constexpr int uu = k / S::USTEP, kk = k % S::USTEP;
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (k % 2 == 0 && k / 2 + DP < S::NPAIR) read_pair(std::integral_constant<int, k / 2 + DP>{});
+    mfma_step(kc);
+    // The next block's tile loads go out once the stream is running, so that the first MFMAs do
+    // not wait behind their issue.
+    if constexpr (k == kDqwIssueStep) issue();
+    elems_at(std::integral_constant<int, uu>{}, std::integral_constant<int, kk>{});
+    if constexpr (uu == 0 && kk == S::USTEP - 1)
+      elems_at(std::integral_constant<int, 1>{}, std::integral_constant<int, -1>{});
+  });
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// After the last key block (at byte offset offl from the first K buffer; key0 = its second
+// sub-block's first key - coff): the dS
+// arithmetic of that sub-block beside the dQ products of the first, then the dQ products of the
+// second.
+template <int E, int D, bool CAUSAL>
+__device__ __forceinline__ void dqw_drain(const DqwAddr<D>& ad, uint32_t offl, int key0, int nk, const int (&qrow)[2],
+                                          int lane, float sl2, const float (&lse)[2], const float (&dlt)[2],
+                                          DqwState<D>& st) {
+  constexpr int DT = D / 32;
+  constexpr int NP = 4 * DT;  // operand reads: 2 DT per sub-block
+  const int hh = lane >> 5;
+  const int lim[2] = {dqw_lim<CAUSAL>(qrow[0], key0, nk, hh), dqw_lim<CAUSAL>(qrow[1], key0, nk, hh)};
+  float tmp = 0.f;
+  e16x8 ring[NP];
+  __builtin_amdgcn_sched_barrier(0);
+  static_for<0, NP>([&](auto pc) __attribute__((always_inline)) {
+    constexpr int p = decltype(pc)::value;
+    constexpr int sb = p / (2 * DT), kh = (p % (2 * DT)) / DT, dt = p % DT;
+    const uint32_t o = offl + (32 * sb + 16 * kh) * 2 * D;
+    ring[p] = lds_ld_tr(ad.tk[dt][0] + o, ad.tk[dt][1] + o);
+  });
+  asm volatile("s_nop 7\n\ts_nop 3");  // as at the start of an iteration
+  __builtin_amdgcn_sched_barrier(0);
+  static_for<0, 2 * NP>([&](auto kc) __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
+    constexpr int p = k / 2, h = k % 2, sb = p / (2 * DT), kh = (p % (2 * DT)) / DT, dt = p % DT, o = 4 * kh;
+    __builtin_amdgcn_sched_barrier(0);
+    st.acc[h][dt] = mfma32x32x16<E>(
+        ring[p], make_e16x8(st.pds[sb][h][o], st.pds[sb][h][o + 1], st.pds[sb][h][o + 2], st.pds[sb][h][o + 3]),
+        st.acc[h][dt]);
+    if constexpr (sb == 0) {
+      static_for<0, 2>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int e = 2 * k + decltype(ic)::value;
+        dqw_elem<E, D, true, 1, e / 16, e % 16>(st, sl2, lse[e / 16], dlt[e / 16], lim[e / 16], tmp);
+      });
+    }
+  });
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int E, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void dqw_kernel(BwdArgs a) {
+  constexpr int BC = kDqwBc, BR = kDqwBr, KS = D / 16, DT = D / 32;
+  constexpr int NB = kDqwBuf;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[NB][BC * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[NB][BC * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hh = lane >> 5;
+
+  int bh, rank;
+  map_block(blockIdx.x, a.BH, a.n_tiles, bh, rank);
+  const int qt = CAUSAL ? a.n_tiles - 1 - rank : rank;
+  const int Nq = a.Nq, Nk = a.Nk;
+  const int q0 = qt * BR;
+  const int64_t qoff = (int64_t)bh * Nq * D;
+  const int64_t koff = (int64_t)bh * Nk * D;
+  const uint16_t* Kg = a.k + koff;
+  const uint16_t* Vg = a.v + koff;
+  const int qw0 = q0 + wave * 64;
+
+  DqwState<D> st;
+  int qrow[2];
+  float lse[2], dlt[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    qrow[h] = qw0 + 32 * h + (lane & 31);
+    const int qsrc = min(qrow[h], Nq - 1);
+    const uint16_t* qs = a.q + qoff + (int64_t)qsrc * D + 8 * hh;
+    const uint16_t* gs = a.dO + qoff + (int64_t)qsrc * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      st.qf[h][ks] = as_e16x8(*reinterpret_cast<const i32x4*>(qs + 16 * ks));
+      st.gf[h][ks] = as_e16x8(*reinterpret_cast<const i32x4*>(gs + 16 * ks));
+    }
+    lse[h] = a.lse[(int64_t)bh * Nq + qsrc] * kLog2e;
+    if (a.fuse_delta) {
+      // delta = sum_c dO[row, c] O[row, c] (fp32) from this lane's half of the row (the other half
+      // sits in lane l ^ 32), stored for the dK/dV kernel, which runs after this one.
+      const uint16_t* os = a.o + qoff + (int64_t)qsrc * D + 8 * hh;
+      float acc = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const i32x4 ov = *reinterpret_cast<const i32x4*>(os + 16 * ks);
+        const i32x4 gv = __builtin_bit_cast(i32x4, st.gf[h][ks]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x2 o2 = unpack2<E>((uint32_t)ov[i]);
+          const f32x2 g2 = unpack2<E>((uint32_t)gv[i]);
+          acc = fmaf(o2[0], g2[0], acc);
+          acc = fmaf(o2[1], g2[1], acc);
+        }
+      }
+      dlt[h] = acc + __shfl_xor(acc, 32, 64);
+      if (hh == 0 && qrow[h] < Nq) a.delta[(int64_t)bh * Nq + qrow[h]] = dlt[h];
+    } else {
+      dlt[h] = a.delta[(int64_t)bh * Nq + qsrc];
+    }
+  }
+
+  // The fragments are only ever the B operand of the inline-asm MFMAs, which take it from
+  // accumulation registers.  Moving them there once, here, keeps the compiler from writing them
+  // just before such an MFMA, which it does not know must wait for the write.
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+a"(st.qf[h][ks]), "+a"(st.gf[h][ks]));
+
+  int n_kv = (Nk + BC - 1) / BC;
+  if (CAUSAL) n_kv = min(n_kv, blocks_through(q0 + BR - 1 + a.coff, BC));
+  const int n_plain = min(n_kv, CAUSAL ? min(blocks_within(q0 + a.coff, BC), Nk / BC) : Nk / BC);
+
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) st.acc[h][dt] = zero16();
+    st.s[1][h] = zero16();
+    st.dp[1][h] = zero16();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.pds[0][h][i] = 0u;
+  }
+
+  // Block j lives in buffer (j + p0) % 4, p0 chosen so that the unrolled plain loop starts in
+  // buffer 0 after the n_plain % 4 leading plain iterations; the masked iterations then start in
+  // buffer 0 as well, and every iteration knows its buffers at compile time.
+  const int rem = n_plain % NB;
+  const int p0 = (NB - rem) % NB;
+  DirectStage<BC, D, kThreads> stg;
+  stg.init(tid);
+  constexpr uint32_t kTileBytes = BC * D * 2;
+  const uint32_t aK = lds_addr(&sK[0][0]), aV = lds_addr(&sV[0][0]);
+  DqwAddr<D> ad;
+  ad.init(aK, aV, lane);
+  {
+    // The K buffer of block -1, read by the first iteration's neutral dQ products.
+    i32x4* z = reinterpret_cast<i32x4*>(&sK[(p0 + NB - 1) % NB][0]);
+#pragma unroll
+    for (int i = 0; i < BC * D * 2 / 16 / kThreads; ++i) z[i * kThreads + tid] = i32x4{0, 0, 0, 0};
+  }
+  if (n_kv > 0) {
+    stg.issue(Kg, 0, Nk, aK + p0 * kTileBytes);
+    stg.issue(Vg, 0, Nk, aV + p0 * kTileBytes);
+  }
+  wait_vm0();
+  __syncthreads();
+
+  float lsep[2] = {__builtin_inff(), __builtin_inff()};
+  int j = 0;
+  auto iter = [&](auto mask_tag, auto buf_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int B = decltype(buf_tag)::value;
+    dqw_iter<E, D, CAUSAL, MASK, B>(ad, j * BC - a.coff, Nk - a.coff, qrow, lane, a.sl2, lse, lsep, dlt, st,
+                                    [&]() __attribute__((always_inline)) {
+                                      if (j + 1 < n_kv) {
+                                        stg.issue(Kg, (j + 1) * BC, Nk, aK + ((B + 1) % NB) * kTileBytes);
+                                        stg.issue(Vg, (j + 1) * BC, Nk, aV + ((B + 1) % NB) * kTileBytes);
+                                      }
+                                    });
+    wait_vm0();
+    __syncthreads();
+    lsep[0] = lse[0];
+    lsep[1] = lse[1];
+    ++j;
+  };
+  using plain = std::integral_constant<bool, false>;
+  using masked = std::integral_constant<bool, true>;
+  using buf0 = std::integral_constant<int, 0>;
+  using buf1 = std::integral_constant<int, 1>;
+  using buf2 = std::integral_constant<int, 2>;
+  if (rem >= 2) iter(plain{}, buf1{});
+  if (rem >= 1) iter(plain{}, buf2{});
+  while (j < n_plain) {
+    iter(plain{}, buf0{});
+    iter(plain{}, buf1{});
+    iter(plain{}, buf2{});
+  }
+  while (j < n_kv) {
+    iter(masked{}, buf0{});
+    if (j < n_kv) iter(masked{}, buf1{});
+    if (j < n_kv) iter(masked{}, buf2{});
+  }
+  if (n_kv > 0) {
+    dqw_drain<E, D, CAUSAL>(ad, ((n_kv - 1 + p0) % NB) * kTileBytes, (n_kv - 1) * BC + 32 - a.coff, Nk - a.coff, qrow,
+                            lane, a.sl2, lse, dlt, st);
+    __syncthreads();  // the drain's reads of the K buffer are done before it becomes the stage area
+  }
+
+  // dQ rows of this wave's 64 queries, 32 at a time through a stage area in the K buffers.
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    store_rows_via_lds<E, D>(reinterpret_cast<uint8_t*>(&sK[0][0]) + wave * (64 * D),
+                             a.dq + qoff + (int64_t)(qw0 + 32 * h) * D, Nq - (qw0 + 32 * h), lane,
+                             [&](int dt, int r) { return st.acc[h][dt][r] * a.scale; });
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -598,15 +996,15 @@ hipError_t launch_bwd_delta(BwdArgs a, int d, hipStream_t s) {
 
 template <int E>
 hipError_t launch_bwd_dq(BwdArgs a, int d, bool causal, hipStream_t s) {
-  a.n_tiles = (a.Nq + kDqBr - 1) / kDqBr;
+  a.n_tiles = (a.Nq + (d == 64 ? kDqBr : kDqwBr) - 1) / (d == 64 ? kDqBr : kDqwBr);
   if (a.n_tiles == 0 || a.BH == 0) return hipSuccess;
   const dim3 grid(a.n_tiles * a.BH);
   if (d == 64) {
     if (causal) hipLaunchKernelGGL((dq_kernel<E, 64, true>), grid, dim3(kThreads), 0, s, a);
     else hipLaunchKernelGGL((dq_kernel<E, 64, false>), grid, dim3(kThreads), 0, s, a);
   } else {
-    if (causal) hipLaunchKernelGGL((dq_kernel<E, 128, true>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((dq_kernel<E, 128, false>), grid, dim3(kThreads), 0, s, a);
+    if (causal) hipLaunchKernelGGL((dqw_kernel<E, 128, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((dqw_kernel<E, 128, false>), grid, dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }
