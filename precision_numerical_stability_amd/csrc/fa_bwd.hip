@@ -685,8 +685,10 @@ struct DkvFrags {
 //   phase 2t + 1     S/dP of sub-block t + 1          (t = 0 .. SB - 2)
 //   phase 2t + 2     dV/dK of sub-block t             (t = 0 .. SB - 2)
 //   phase 2 SB - 1   dV/dK of sub-block SB - 1
-// An S/dP step is one MFMA (k-slice ks = i / 2 of S when i is even, of dP when odd) with one
-// 16-byte operand read; a dV/dK step is one MFMA (half i / (2 D/32), d-tile (i / 2) % (D/32), dV
+// An S/dP step is one MFMA (k-slice ks = i of S for i < D/16, then k-slice i - D/16 of dP) with
+// one 16-byte operand read; the first dP step starts from -delta of the sub-block's queries (read
+// from LDS as a 16-register tile at the phase's first step), so dP - delta comes out of the
+// MFMAs; a dV/dK step is one MFMA (half i / (2 D/32), d-tile (i / 2) % (D/32), dV
 // when i is even, dK when odd) with one transposed operand read.  The softmax-gradient arithmetic
 // of half g of the block (sub-block g / 2, query rows 16 (g % 2) .. + 15 of it; 8 elements per lane)
 // runs element by element beside the MFMAs: halves 0 and 1 in phase 1, half g in phase g after
@@ -724,7 +726,7 @@ struct DkvSched {
     if (p % 2 == 1) return 8 * p + ((L == 16) ? j / 2 : j);
     return 8 * p + ((L == 16) ? (j - 1) / 2 : j);
   }
-  // Halves whose LSE/delta vectors are read from LDS at step k: returns a bit mask over g.  Half
+  // Halves whose LSE vectors are read from LDS at step k: returns a bit mask over g.  Half
   // g + 1 is read at the start of phase g, a whole phase ahead of its use (its register slot's
   // previous half, g - 1, finished in phase g - 1), except in phase 1, which runs halves 0 and 1:
   // there half 2 is read once half 0, which still uses that slot, is done (step L / 2).
@@ -752,15 +754,17 @@ __device__ __forceinline__ void dkdv_block(const uint16_t* tQ, const uint16_t* t
   f32x16 s[2], dp[2];
   uint32_t pp[2][8], pd[2][8];
   e16x8 ring[RING];
-  float4 lsl[2][2], dsl[2][2];  // [half slot][row group] LSE (log2 units) and delta vectors
+  float4 lsl[2][2];  // [half slot][row group] LSE (log2 units)
+  f32x16 nd;         // -delta tile of the sub-block whose S/dP phase runs
   float pt0 = 0.f, dt0 = 0.f;   // first element of the pair being packed
 
   auto read_op = [&](auto kc) __attribute__((always_inline)) {
     constexpr int k = decltype(kc)::value;
     constexpr int t = S::sub(k), i = k % S::L;
     if constexpr (S::is_sdp(k)) {
-      constexpr int ks = i >> 1;
-      ring[k % RING] = lds_read_row8<D>((i & 1) ? tG : tQ, 32 * t + l32, 16 * ks + 8 * hh);
+      constexpr bool is_dp = i >= D / 16;
+      constexpr int ks = is_dp ? i - D / 16 : i;
+      ring[k % RING] = lds_read_row8<D>(is_dp ? tG : tQ, 32 * t + l32, 16 * ks + 8 * hh);
     } else {
       constexpr int half = i / (2 * DT), dt = (i >> 1) % DT;
       ring[k % RING] = lds_read_col8_tr<D>((i & 1) ? tQ : tG, 32 * t + 16 * half, 32 * dt, lane);
@@ -773,7 +777,19 @@ __device__ __forceinline__ void dkdv_block(const uint16_t* tQ, const uint16_t* t
     for (int w = 0; w < 2; ++w) {
       const int qi = 32 * t + 8 * (2 * h + w) + 4 * hh;
       lsl[g & 1][w] = *reinterpret_cast<const float4*>(&tL[qi]);
-      dsl[g & 1][w] = *reinterpret_cast<const float4*>(&tD[qi]);
+    }
+  };
+  // -delta of sub-block t's queries in the accumulator layout (register r: query 32 t + 8 (r / 4)
+  // + 4 h + r % 4), the C operand of its first dP MFMA.
+  auto read_nd = [&](auto tc) __attribute__((always_inline)) {
+    constexpr int t = decltype(tc)::value;
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const float4 v = *reinterpret_cast<const float4*>(&tD[32 * t + 8 * rq + 4 * hh]);
+      nd[4 * rq] = v.x;
+      nd[4 * rq + 1] = v.y;
+      nd[4 * rq + 2] = v.z;
+      nd[4 * rq + 3] = v.w;
     }
   };
   auto mfma_step = [&](auto kc) __attribute__((always_inline)) {
@@ -781,11 +797,14 @@ __device__ __forceinline__ void dkdv_block(const uint16_t* tQ, const uint16_t* t
     constexpr int t = S::sub(k), i = k % S::L, c = t & 1;
     const e16x8 op = ring[k % RING];
     if constexpr (S::is_sdp(k)) {
-      constexpr int ks = i >> 1;
-      if constexpr ((i & 1) == 0) {
+      constexpr bool is_dp = i >= D / 16;
+      constexpr int ks = is_dp ? i - D / 16 : i;
+      if constexpr (!is_dp) {
         s[c] = mfma32x32x16_vgpr<E, ks == 0>(op, f.k[ks], s[c]);
+      } else if constexpr (ks == 0) {
+        dp[c] = mfma32x32x16_vgpr_from<E>(op, f.v[0], nd);
       } else {
-        dp[c] = mfma32x32x16_vgpr<E, ks == 0>(op, f.v[ks], dp[c]);
+        dp[c] = mfma32x32x16_vgpr<E, false>(op, f.v[ks], dp[c]);
       }
     } else {
       constexpr int half = i / (2 * DT), dt = (i >> 1) % DT, o4 = 4 * half;
@@ -805,9 +824,7 @@ __device__ __forceinline__ void dkdv_block(const uint16_t* tQ, const uint16_t* t
     constexpr int t = g >> 1, h = g & 1, c = t & 1;
     constexpr int w = e >> 2, rq = 2 * h + w, u = e & 3, r = 4 * rq + u;
     const float4 l4 = lsl[g & 1][w];
-    const float4 d4 = dsl[g & 1][w];
     const float lv = u == 0 ? l4.x : u == 1 ? l4.y : u == 2 ? l4.z : l4.w;
-    const float dl = u == 0 ? d4.x : u == 1 ? d4.y : u == 2 ? d4.z : d4.w;
     float p = fast_exp2(fmaf(s[c][r], sl2, -lv));
     if (MASK) {
       // Query q0 + c + 4 hh, c = 32 t + 8 rq + u, is hidden past Nq or (causal) before
@@ -818,7 +835,7 @@ __device__ __forceinline__ void dkdv_block(const uint16_t* tQ, const uint16_t* t
       constexpr int c = 32 * t + 8 * rq + u;
       p = (c > hi || c < lo) ? 0.f : p;
     }
-    const float ds = p * (dp[c][r] - dl);
+    const float ds = p * dp[c][r];  // dP - delta
     if constexpr ((u & 1) == 0) {
       pt0 = p;
       dt0 = ds;
@@ -834,6 +851,7 @@ __device__ __forceinline__ void dkdv_block(const uint16_t* tQ, const uint16_t* t
     constexpr int k = decltype(kc)::value;
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (k + DEPTH < S::NSTEP) read_op(std::integral_constant<int, k + DEPTH>{});
+    if constexpr (S::is_sdp(k) && k % S::L == 0) read_nd(std::integral_constant<int, S::sub(k)>{});
     constexpr int ldm = S::ld_halves(k);
     static_for<0, 2 * S::SB>([&](auto gc) __attribute__((always_inline)) {
       if constexpr ((ldm >> decltype(gc)::value) & 1) read_ld(gc);
@@ -913,7 +931,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   auto store_rows = [&](int b) __attribute__((always_inline)) {
     if (tid < BQ) {
       sL[b][tid] = vl * kLog2e;
-      sD[b][tid] = vd;
+      sD[b][tid] = -vd;  // the dP products start from -delta
     }
   };
 

@@ -88,6 +88,16 @@ __device__ __forceinline__ f32x16 mfma32x32x16_vgpr(e16x8 a, e16x8 b_acc, f32x16
   return d;
 }
 
+// As mfma32x32x16_vgpr, accumulating onto c into a distinct destination: c stays live (the
+// destination is early-clobber, so it overlaps none of the inputs).
+template <int E>
+__device__ __forceinline__ f32x16 mfma32x32x16_vgpr_from(e16x8 a, e16x8 b_acc, f32x16 c) {
+  f32x16 d;
+  if constexpr (E == kElemF16) asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b_acc), "v"(c));
+  else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b_acc), "v"(c));
+  return d;
+}
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
