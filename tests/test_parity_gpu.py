@@ -521,18 +521,19 @@ def test_square_alignments_agree(fa, causal):
         assert torch.equal(a, b)
 
 
-def test_no_keys_and_no_queries(fa):
-    _say("rect-empty")
-    q = torch.randn((1, 2, 70, 64), device=DEV).to(torch.bfloat16)
-    kv0 = torch.empty((1, 2, 0, 64), dtype=torch.bfloat16, device=DEV)
+@pytest.mark.parametrize("d", [64, 128])
+def test_no_keys_and_no_queries(fa, d):
+    _say("rect-empty", d)
+    q = torch.randn((1, 2, 70, d), device=DEV).to(torch.bfloat16)
+    kv0 = torch.empty((1, 2, 0, d), dtype=torch.bfloat16, device=DEV)
     for causal in (0, 1, 2):
         o, lse = fa.forward(q, kv0, kv0, causal, 0.125)
         dq, dk, dv = fa.backward(q, kv0, kv0, o, lse, q, causal, 0.125)
         torch.cuda.synchronize()
         assert torch.all(o == 0) and torch.all(lse == -float("inf")) and torch.all(dq == 0)
         assert dk.numel() == 0 and dv.numel() == 0
-    k = torch.randn((1, 2, 90, 64), device=DEV).to(torch.bfloat16)
-    q0 = torch.empty((1, 2, 0, 64), dtype=torch.bfloat16, device=DEV)
+    k = torch.randn((1, 2, 90, d), device=DEV).to(torch.bfloat16)
+    q0 = torch.empty((1, 2, 0, d), dtype=torch.bfloat16, device=DEV)
     o, lse = fa.forward(q0, k, k, 2, 0.125)
     dk = torch.full_like(k, 7.0)
     dv = torch.full_like(k, 7.0)
